@@ -1,0 +1,210 @@
+/*
+ * rba_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously-correct CPU reference for paged attention with a
+ * learned relative-position bias.  Only tests/, the smoke check and the
+ * cpu_baseline leg of bench.py may load this library; the product path never
+ * does.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What is computed (one query row at a time, in fp64, on the inputs exactly
+ * as stored -- bf16 and fp32 widen to double without rounding):
+ *
+ *   score[s] = sm_scale * <q[t,h,:], k[s,g,:]> + bias[t,h,min(t-s, R-1)]
+ *                                       if s <= t and (W <= 0 or t-s < W)
+ *   score[s] = -inf                     otherwise
+ *   p[s]     = exp(score[s] - max score),  l = sum p,
+ *   out[t,h] = sum_s p[s] v[s,g,:] / l,    lse[t,h] = max score + ln l
+ *
+ * Sources (TensorRT-LLM PR #17062 "Support Inkling-NVFP4 model", and
+ * TensorRT-LLM PR #17860 "Inkling attn backend cleanup fake registry"):
+ *  - the bias is added before the softmax and is indexed by
+ *    (query token, head, relative distance): PR #17062, Description,
+ *    "Architecture" list, first item;
+ *  - local layers attend a causal sliding window, global layers are full
+ *    causal (window_left = -1): PR #17062 "Architecture", second item, and the
+ *    PR #17860 commit that tests the sm_scale / rel_extent / window_left
+ *    hand-off;
+ *  - the bias tensor is [T, heads, rel_extent], one row per query token and
+ *    head, rel_extent = 1024 on a global layer: PR #17062 review comment on
+ *    _build_rel_logits; it is projected per query token, not a per-head bucket
+ *    table: PR #17860, the commit that moves four hand-rolled pieces onto the
+ *    framework's existing hooks, item 2;
+ *  - query head h reads KV head h / (Hq / Hkv), Hq divisible by Hkv:
+ *    PR #17860 commit that makes both Triton entry points assert it;
+ *  - distances past the last bucket share bucket R-1 (clamp) and the bias is
+ *    added to the already-scaled q.k: the plainest reading of "rel_extent"
+ *    together with the per-distance indexing above.
+ *
+ * The reference reads K and V from logical (un-paged) tensors, token-major,
+ * so it never touches a page table.
+ *
+ * Parity of every function here is pinned by the CPU tests in tests/
+ * (brute force, closed forms, invariants, library special cases).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+/* Widen element i of a tensor stored as fp32 or bf16 to double (exact). */
+static double elem(const void *base, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float *)base)[i];
+  uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/*
+ * One output row.  t is the query position inside its sequence, n_keys the
+ * number of keys held for the sequence (keys 0 .. n_keys-1).  q_row, bias_row
+ * are element offsets of the query vector and of the bias row; kv0 is the
+ * element offset of key 0 / head 0 in the logical K and V tensors, whose row
+ * stride is Hkv*D.  scores is scratch of n_keys doubles.
+ */
+static void attend_row(int dtype, const void *q, int64_t q_row, const void *k,
+                       const void *v, int64_t kv0, int Hkv, int D, int g,
+                       int64_t t, int64_t n_keys, const void *bias,
+                       int64_t bias_row, int R, int W, double sm_scale,
+                       double *scores, double *out, double *lse) {
+  const int64_t kv_stride = (int64_t)Hkv * D;
+  double m = -INFINITY;
+  for (int64_t s = 0; s < n_keys; ++s) {
+    int visible = (s <= t) && (W <= 0 || t - s < W);
+    if (!visible) {
+      scores[s] = -INFINITY;
+      continue;
+    }
+    double dot = 0.0;
+    for (int i = 0; i < D; ++i)
+      dot += elem(q, dtype, q_row + i) *
+             elem(k, dtype, kv0 + s * kv_stride + (int64_t)g * D + i);
+    int64_t d = t - s;
+    if (d > R - 1) d = R - 1;
+    scores[s] = sm_scale * dot + elem(bias, dtype, bias_row + d);
+    if (scores[s] > m) m = scores[s];
+  }
+  for (int i = 0; i < D; ++i) out[i] = 0.0;
+  if (m == -INFINITY) { /* no visible key: defined as a zero row */
+    if (lse) *lse = -INFINITY;
+    return;
+  }
+  double l = 0.0;
+  for (int64_t s = 0; s < n_keys; ++s) {
+    if (scores[s] == -INFINITY) continue;
+    double p = exp(scores[s] - m);
+    l += p;
+    for (int i = 0; i < D; ++i)
+      out[i] += p * elem(v, dtype, kv0 + s * kv_stride + (int64_t)g * D + i);
+  }
+  for (int i = 0; i < D; ++i) out[i] /= l;
+  if (lse) *lse = m + log(l);
+}
+
+static int set_threads(int num_threads) {
+#ifdef _OPENMP
+  if (num_threads > 0) omp_set_num_threads(num_threads);
+  return omp_get_max_threads();
+#else
+  (void)num_threads;
+  return 1;
+#endif
+}
+
+/*
+ * Prefill: every sequence b holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1,
+ * each token is a query at position t = token - cu_seqlens[b] and also the key
+ * at that position.  q [T,Hq,D], k/v [T,Hkv,D], bias [T,Hq,R].
+ * rows: optional list of n_rows (token, head) pairs; NULL means all T*Hq rows
+ * in (token, head) order.  out [n_rows, D] fp64, lse [n_rows] fp64 (nullable).
+ * Returns the number of threads used, or -1 on a bad argument.
+ */
+int rba_oracle_prefill(int dtype, const void *q, const void *k, const void *v,
+                       const void *bias, const int64_t *cu_seqlens,
+                       int num_seqs, int Hq, int Hkv, int D, int R, int W,
+                       double sm_scale, const int64_t *rows, int64_t n_rows,
+                       double *out, double *lse, int num_threads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || R < 1 || num_seqs < 0) return -1;
+  const int G = Hq / Hkv;
+  const int64_t T = cu_seqlens[num_seqs];
+  int64_t max_len = 0;
+  for (int b = 0; b < num_seqs; ++b)
+    if (cu_seqlens[b + 1] - cu_seqlens[b] > max_len)
+      max_len = cu_seqlens[b + 1] - cu_seqlens[b];
+  if (!rows) n_rows = T * Hq;
+  int used = set_threads(num_threads);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *scores = (double *)malloc(sizeof(double) * (size_t)(max_len + 1));
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t tok = rows ? rows[2 * r] : r / Hq;
+      int h = rows ? (int)rows[2 * r + 1] : (int)(r % Hq);
+      if (tok < 0 || tok >= T || h < 0 || h >= Hq) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      int b = 0;
+      while (cu_seqlens[b + 1] <= tok) ++b;
+      int64_t start = cu_seqlens[b];
+      int64_t len = cu_seqlens[b + 1] - start;
+      attend_row(dtype, q, (tok * Hq + h) * (int64_t)D, k, v,
+                 start * (int64_t)Hkv * D, Hkv, D, h / G, tok - start, len,
+                 bias, (tok * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
+                 out + r * (int64_t)D, lse ? lse + r : NULL);
+    }
+    free(scores);
+  }
+  return bad ? -1 : used;
+}
+
+/*
+ * Decode: one query per sequence, at position n_b - 1, where n_b is the number
+ * of keys held for sequence b (the current token's key included).
+ * q [B,Hq,D]; k/v hold the keys of all B sequences back to back, sequence b at
+ * rows cu_kv[b] .. cu_kv[b+1]-1 of a [sum n_b, Hkv, D] tensor; bias [B,Hq,R].
+ * rows: optional (sequence, head) pairs; NULL means all B*Hq rows.
+ */
+int rba_oracle_decode(int dtype, const void *q, const void *k, const void *v,
+                      const void *bias, const int64_t *cu_kv, int num_seqs,
+                      int Hq, int Hkv, int D, int R, int W, double sm_scale,
+                      const int64_t *rows, int64_t n_rows, double *out,
+                      double *lse, int num_threads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || R < 1 || num_seqs < 0) return -1;
+  const int G = Hq / Hkv;
+  int64_t max_len = 0;
+  for (int b = 0; b < num_seqs; ++b)
+    if (cu_kv[b + 1] - cu_kv[b] > max_len) max_len = cu_kv[b + 1] - cu_kv[b];
+  if (!rows) n_rows = (int64_t)num_seqs * Hq;
+  int used = set_threads(num_threads);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *scores = (double *)malloc(sizeof(double) * (size_t)(max_len + 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t b = rows ? rows[2 * r] : r / Hq;
+      int h = rows ? (int)rows[2 * r + 1] : (int)(r % Hq);
+      if (b < 0 || b >= num_seqs || h < 0 || h >= Hq) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      int64_t n = cu_kv[b + 1] - cu_kv[b];
+      attend_row(dtype, q, (b * Hq + h) * (int64_t)D, k, v,
+                 cu_kv[b] * (int64_t)Hkv * D, Hkv, D, h / G, n - 1, n, bias,
+                 (b * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
+                 out + r * (int64_t)D, lse ? lse + r : NULL);
+    }
+    free(scores);
+  }
+  return bad ? -1 : used;
+}

@@ -1,0 +1,301 @@
+"""Seeded synthetic inputs for relative-position-bias paged attention.
+
+This module only draws random tensors and lays them out; it computes nothing
+of the attention itself.  Both the HIP library's callers (tests, bench, smoke)
+and the CPU oracle take their inputs from here.
+
+Layouts produced (the C ABI in include/rba.h documents the same):
+  q        [T, Hq, D]  (prefill, tokens of all sequences back to back)
+           [B, Hq, D]  (decode, one query per sequence)
+  bias     [T, Hq, R] / [B, Hq, R]
+  k_pool, v_pool  [num_pages, Hkv, P, D], one page = P consecutive key
+           positions of one sequence, head-major inside the page
+  block_table     int32 [B, max_pages]; entry j is the pool page holding key
+           positions j*P .. j*P+P-1; entries past a sequence's last page are 0
+  seq_lens        int32 [B]; keys held for each sequence
+  k_log, v_log    logical K/V, token-major [sum_b n_b, Hkv, D], for the oracle
+
+Recipe: float tensors are N(0,1) (the tiny fp32 case draws its bias with
+standard deviation 0.5) and are cast to the workload dtype before either side
+sees them.  Page placements and context lengths come from a CPU generator with
+the workload's seed.  Pool pages that no sequence owns, and the slots past the
+end of a sequence's last page, are filled with NaN so that a stray read shows
+up in the output.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import torch
+
+POISON = float("nan")
+
+
+@dataclasses.dataclass
+class LayerSpec:
+    """One attention layer's geometry."""
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    window: int          # <= 0: full causal
+    rel_extent: int
+    page_size: int
+    dtype: torch.dtype = torch.bfloat16
+    sm_scale: Optional[float] = None
+    bias_std: float = 1.0
+
+    def scale(self) -> float:
+        return self.sm_scale if self.sm_scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+
+@dataclasses.dataclass
+class PrefillCase:
+    spec: LayerSpec
+    seq_lens: List[int]
+    q: torch.Tensor
+    k_log: torch.Tensor
+    v_log: torch.Tensor
+    bias: torch.Tensor
+    cu_seqlens: torch.Tensor      # int32 [B+1], device
+    seq_lens_dev: torch.Tensor    # int32 [B], device
+    block_table: torch.Tensor     # int32 [B, max_pages], device
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seq_lens))
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.seq_lens)) if self.seq_lens else 0
+
+    def cu_list(self) -> List[int]:
+        cu = [0]
+        for n in self.seq_lens:
+            cu.append(cu[-1] + n)
+        return cu
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    spec: LayerSpec
+    seq_lens: List[int]
+    q: torch.Tensor
+    bias: torch.Tensor
+    seq_lens_dev: torch.Tensor
+    block_table: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    seed: int
+    window_only: bool
+    _kv_first_page: List[int]     # first page index whose contents are real
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(max(self.seq_lens)) if self.seq_lens else 0
+
+    def logical_kv(self, b: int):
+        """Logical K/V [n_b, Hkv, D] of sequence b, on the CPU.
+
+        Regenerated from the per-sequence seed (same device as the pool, so
+        the values are the ones scattered into the pool); positions whose page
+        is not real (window-only pools) are NaN.
+        """
+        k, v = _seq_kv(self.spec, self.seed, b, self.seq_lens[b], self.q.device)
+        k, v = k.cpu(), v.cpu()
+        first = self._kv_first_page[b] * self.spec.page_size
+        if first > 0:
+            k[:first] = POISON
+            v[:first] = POISON
+        return k, v
+
+
+def _cpu_gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def _dev_gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randn(shape, gen, device, dtype, std=1.0):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(dtype)
+
+
+def _scatter_pages(pool: torch.Tensor, pages: torch.Tensor, kv: torch.Tensor, P: int):
+    """Write logical rows kv [n, Hkv, D] into pool pages ``pages`` (in order)."""
+    n, Hkv, D = kv.shape
+    npg = pages.numel()
+    padded = torch.full((npg * P, Hkv, D), POISON, dtype=kv.dtype, device=kv.device)
+    padded[:n] = kv
+    pool[pages.to(pool.device).long()] = padded.view(npg, P, Hkv, D).permute(0, 2, 1, 3)
+
+
+def make_prefill(spec: LayerSpec, seq_lens: List[int], seed: int, device="cpu",
+                 num_pages: Optional[int] = None, shuffle: bool = True) -> PrefillCase:
+    """Prefill inputs: each sequence's keys are its own tokens (no history)."""
+    P = spec.page_size
+    B = len(seq_lens)
+    T = int(sum(seq_lens))
+    g = _dev_gen(seed, device)
+    q = _randn((T, spec.num_q_heads, spec.head_dim), g, device, spec.dtype)
+    k_log = _randn((T, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    v_log = _randn((T, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    bias = _randn((T, spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
+                  std=spec.bias_std)
+
+    pages_per = [max(1, -(-n // P)) for n in seq_lens]
+    needed = int(sum(pages_per))
+    if num_pages is None:
+        num_pages = needed
+    if num_pages < needed:
+        raise ValueError("pool too small")
+    cg = _cpu_gen(seed)
+    perm = torch.randperm(num_pages, generator=cg) if shuffle else torch.arange(num_pages)
+    max_pages = max(pages_per) if pages_per else 1
+    table = torch.zeros((max(B, 1), max_pages), dtype=torch.int32)
+    k_pool = torch.full((num_pages, spec.num_kv_heads, P, spec.head_dim), POISON,
+                        dtype=spec.dtype, device=device)
+    v_pool = torch.full_like(k_pool, POISON)
+    off = 0
+    tok = 0
+    for b, n in enumerate(seq_lens):
+        pg = perm[off:off + pages_per[b]]
+        table[b, :pages_per[b]] = pg.to(torch.int32)
+        if n > 0:
+            _scatter_pages(k_pool, pg, k_log[tok:tok + n], P)
+            _scatter_pages(v_pool, pg, v_log[tok:tok + n], P)
+        off += pages_per[b]
+        tok += n
+    cu = [0]
+    for n in seq_lens:
+        cu.append(cu[-1] + n)
+    return PrefillCase(
+        spec=spec, seq_lens=list(seq_lens), q=q, k_log=k_log, v_log=v_log, bias=bias,
+        cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device),
+        seq_lens_dev=torch.tensor(list(seq_lens) or [0], dtype=torch.int32, device=device)[:B],
+        block_table=table.to(device), k_pool=k_pool, v_pool=v_pool)
+
+
+def _seq_kv(spec: LayerSpec, seed: int, b: int, n: int, device):
+    g = _dev_gen(seed * 1_000_003 + 7919 * (b + 1), device)
+    k = _randn((n, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    v = _randn((n, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    return k, v
+
+
+def make_decode(spec: LayerSpec, seq_lens: List[int], seed: int, device="cpu",
+                window_only: bool = False, shuffle: bool = True) -> DecodeCase:
+    """Decode inputs: sequence b holds n_b keys; its query sits at n_b - 1.
+
+    With ``window_only`` (local layers) only the pages covering the last
+    ``window`` positions hold real keys; every earlier table entry points to
+    pool page 0, which is NaN-filled and must never influence the output.
+    """
+    P = spec.page_size
+    B = len(seq_lens)
+    g = _dev_gen(seed, device)
+    q = _randn((B, spec.num_q_heads, spec.head_dim), g, device, spec.dtype)
+    bias = _randn((B, spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
+                  std=spec.bias_std)
+
+    pages_per = [max(1, -(-n // P)) for n in seq_lens]
+    first_real = []
+    for n, npg in zip(seq_lens, pages_per):
+        if window_only and spec.window > 0:
+            first_real.append(max(0, n - spec.window) // P)
+        else:
+            first_real.append(0)
+    real_per = [npg - f for npg, f in zip(pages_per, first_real)]
+    reserve = 1 if window_only else 0
+    num_pages = reserve + int(sum(real_per))
+    cg = _cpu_gen(seed)
+    perm = (torch.randperm(num_pages - reserve, generator=cg) if shuffle
+            else torch.arange(num_pages - reserve)) + reserve
+    max_pages = max(pages_per) if pages_per else 1
+    table = torch.zeros((max(B, 1), max_pages), dtype=torch.int32)
+    k_pool = torch.empty((num_pages, spec.num_kv_heads, P, spec.head_dim),
+                         dtype=spec.dtype, device=device)
+    v_pool = torch.empty_like(k_pool)
+    if reserve:
+        k_pool[0] = POISON
+        v_pool[0] = POISON
+    off = 0
+    for b, n in enumerate(seq_lens):
+        pg = perm[off:off + real_per[b]]
+        table[b, first_real[b]:pages_per[b]] = pg.to(torch.int32)
+        k, v = _seq_kv(spec, seed, b, n, device)
+        lo = first_real[b] * P
+        _scatter_pages(k_pool, pg, k[lo:], P)
+        _scatter_pages(v_pool, pg, v[lo:], P)
+        del k, v
+        off += real_per[b]
+    return DecodeCase(
+        spec=spec, seq_lens=list(seq_lens), q=q, bias=bias,
+        seq_lens_dev=torch.tensor(list(seq_lens), dtype=torch.int32, device=device),
+        block_table=table.to(device), k_pool=k_pool, v_pool=v_pool, seed=seed,
+        window_only=window_only, _kv_first_page=first_real)
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads (sizes of the layers described on the pages: local
+# layers window 512 with 16 KV heads, global layers full causal with 8 KV heads
+# and a 1024-bucket bias, 32 query heads, head_dim 128, 64-token pages).
+
+LOCAL = dict(num_q_heads=32, num_kv_heads=16, head_dim=128, window=512,
+             rel_extent=512, page_size=64)
+GLOBAL = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, window=0,
+              rel_extent=1024, page_size=64)
+
+WORKLOADS = {
+    "tiny-local-prefill-fp32": dict(
+        kind="prefill", seed=1001, seq_lens=[256], num_pages=16, shuffle=False,
+        spec=LayerSpec(num_q_heads=4, num_kv_heads=2, head_dim=64, window=64,
+                       rel_extent=64, page_size=16, dtype=torch.float32,
+                       bias_std=0.5)),
+    "local-prefill-4x4096": dict(
+        kind="prefill", seed=1002, seq_lens=[4096] * 4, num_pages=512, shuffle=True,
+        spec=LayerSpec(**LOCAL)),
+    "global-prefill-2x16384": dict(
+        kind="prefill", seed=1003, seq_lens=[16384] * 2, num_pages=512, shuffle=True,
+        spec=LayerSpec(**GLOBAL)),
+    "mixed-decode-256": dict(
+        kind="mixed-decode", seed=1004, batch=256, ctx_lo=1024, ctx_hi=32768,
+        local=LayerSpec(**LOCAL), glob=LayerSpec(**GLOBAL)),
+    "long-decode-32x131072": dict(
+        kind="decode", seed=1005, seq_lens=[131072] * 32, num_splits=16,
+        spec=LayerSpec(**GLOBAL)),
+}
+
+
+def mixed_decode_lengths(seed: int, batch: int, lo: int, hi: int) -> List[int]:
+    """Context lengths uniform in [lo, hi] (inclusive), from the CPU generator."""
+    g = _cpu_gen(seed + 17)
+    return torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+
+
+def build_workload(name: str, device="cpu"):
+    """Materialise a named workload.  Returns a dict of cases."""
+    w = WORKLOADS[name]
+    if w["kind"] == "prefill":
+        return {"prefill": make_prefill(w["spec"], w["seq_lens"], w["seed"], device,
+                                        num_pages=w["num_pages"], shuffle=w["shuffle"])}
+    if w["kind"] == "decode":
+        return {"decode": make_decode(w["spec"], w["seq_lens"], w["seed"], device)}
+    if w["kind"] == "mixed-decode":
+        lens = mixed_decode_lengths(w["seed"], w["batch"], w["ctx_lo"], w["ctx_hi"])
+        return {
+            "local": make_decode(w["local"], lens, w["seed"], device, window_only=True),
+            "global": make_decode(w["glob"], lens, w["seed"] + 100, device),
+        }
+    raise KeyError(name)
