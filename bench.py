@@ -1,0 +1,310 @@
+"""Benchmark of relative-position-bias paged attention on one MI355X.
+
+One step = one pass of the hot path over one batch of the headline workload:
+the local sliding-window layer prefill of 4 sequences x 4096 tokens (32 query
+heads, 16 KV heads, head_dim 128, window 512, bias [T, 32, 512] bf16, 64-token
+pages placed by a shuffled 512-page pool).  Inputs are synthetic, seeded, and
+resident in HBM before timing starts.
+
+Printed: one JSON line with the throughput (prefill TFLOP/s), a roofline
+object for the kernel (achieved algorithmic GB/s against HBM peak, from HIP
+events on the launch stream), the CPU oracle timed on a bounded sample of the
+same workload, and the other four-layer workloads (global-layer prefill,
+mixed and long-context decode) measured more briefly under "secondary".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MAIN = "local-prefill-4x4096"
+SECONDARY = ["global-prefill-2x16384", "mixed-decode-256", "long-decode-32x131072"]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (visible pairs only; every byte counted once)
+
+def visible_prefill_pairs(L: int, W: int) -> int:
+    if W > 0 and L > W:
+        return W * (W + 1) // 2 + (L - W) * W
+    return L * (L + 1) // 2
+
+
+def bias_entries_prefill(L: int, W: int, R: int) -> int:
+    cap = min(W, R) if W > 0 else R
+    if L > cap:
+        return cap * (cap + 1) // 2 + (L - cap) * cap
+    return L * (L + 1) // 2
+
+
+def prefill_work(case):
+    sp = case.spec
+    D, Hq, Hkv, W, R = sp.head_dim, sp.num_q_heads, sp.num_kv_heads, sp.window, sp.rel_extent
+    es = 2 if str(sp.dtype) == "torch.bfloat16" else 4
+    pairs = sum(visible_prefill_pairs(L, W) for L in case.seq_lens)
+    T = case.total_tokens
+    flops = 4 * D * Hq * pairs
+    byt = (T * Hq * D * es * 2                      # q read, out written
+           + T * Hkv * D * es * 2                   # k, v
+           + Hq * es * sum(bias_entries_prefill(L, W, R) for L in case.seq_lens))
+    return flops, byt
+
+
+def decode_work(case):
+    sp = case.spec
+    D, Hq, Hkv, W, R = sp.head_dim, sp.num_q_heads, sp.num_kv_heads, sp.window, sp.rel_extent
+    es = 2
+    flops = 0
+    byt = 0
+    for n in case.seq_lens:
+        vis = min(n, W) if W > 0 else n
+        flops += 4 * D * Hq * vis
+        byt += vis * Hkv * D * es * 2 + Hq * min(vis, R) * es
+    B = len(case.seq_lens)
+    byt += B * Hq * D * es * 2
+    return flops, byt
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "relative_position_bias_paged_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, kernel_source: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("source_sha256") != source_hash(kernel_source):
+        return None
+    return rec.get("traffic_bytes")
+
+
+# ---------------------------------------------------------------------------
+# timing
+
+def time_steps(step, steps: int, warmup: int, torch):
+    """Run warmup, then `steps` timed steps.  Returns (wall ms per step,
+    mean event ms per launch of the timed steps)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        step()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    return wall, ev
+
+
+def cpu_baseline(case, budget_s: float):
+    """The oracle, as it stands, on a random sample of the workload's rows."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    sp = case.spec
+    cu = case.cu_list()
+    q, k, v, bias = case.q.cpu(), case.k_log.cpu(), case.v_log.cpu(), case.bias.cpu()
+    g = torch.Generator().manual_seed(12345)
+    T, Hq = case.total_tokens, sp.num_q_heads
+
+    def rows_flops(rows):
+        f = 0
+        for tok, _ in rows:
+            b = int(np.searchsorted(cu, tok, side="right")) - 1
+            t = tok - cu[b]
+            vis = min(t + 1, sp.window) if sp.window > 0 else t + 1
+            f += 4 * sp.head_dim * vis
+        return f
+
+    def draw(n):
+        toks = torch.randint(0, T, (n,), generator=g).tolist()
+        hs = torch.randint(0, Hq, (n,), generator=g).tolist()
+        return list(zip(toks, hs))
+
+    orc = oracle.default()
+    probe = draw(256)
+    t0 = time.perf_counter()
+    orc.prefill(q, k, v, bias, cu, window=sp.window, rel_extent=sp.rel_extent,
+                sm_scale=sp.scale(), rows=probe)
+    dt = time.perf_counter() - t0
+    n = max(256, int(256 * budget_s / max(dt, 1e-3)))
+    rows = draw(n)
+    t0 = time.perf_counter()
+    orc.prefill(q, k, v, bias, cu, window=sp.window, rel_extent=sp.rel_extent,
+                sm_scale=sp.scale(), rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": rows_flops(rows) / dt / 1e12, "unit": "TFLOP/s",
+            "cores": orc.threads_used, "kind": "oracle",
+            "sample": f"{n} random (token, head) rows of {T * Hq}; fp64, full score rows, "
+                      f"{dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+
+def run_prefill(case, steps, warmup, torch, rba):
+    sp = case.spec
+    out = torch.empty_like(case.q)
+
+    def step():
+        rba.prefill(case.q, case.cu_seqlens, case.max_seqlen, case.k_pool, case.v_pool,
+                    case.block_table, case.seq_lens_dev, case.bias, window=sp.window,
+                    sm_scale=sp.scale(), out=out)
+
+    return time_steps(step, steps, warmup, torch)
+
+
+def run_decode(cases, splits, steps, warmup, torch, rba):
+    ws = {}
+    outs = {}
+    for key, c in cases.items():
+        sp = c.spec
+        need = rba.decode_workspace_size(c.q, c.k_pool, c.v_pool, c.block_table, c.seq_lens_dev,
+                                         c.max_seq_len, c.bias, window=sp.window,
+                                         sm_scale=sp.scale(), num_splits=splits)
+        ws[key] = torch.empty(max(need, 1), dtype=torch.uint8, device=c.q.device)
+        outs[key] = torch.empty_like(c.q)
+
+    def step():
+        for key, c in cases.items():
+            sp = c.spec
+            rba.decode(c.q, c.k_pool, c.v_pool, c.block_table, c.seq_lens_dev, c.max_seq_len,
+                       c.bias, window=sp.window, sm_scale=sp.scale(), num_splits=splits,
+                       workspace=ws[key], out=outs[key])
+
+    return time_steps(step, steps, warmup, torch)
+
+
+def secondary(name, torch, rba, ri, steps, warmup):
+    w = ri.WORKLOADS[name]
+    cases = ri.build_workload(name, torch.device("cuda:0"))
+    if w["kind"] == "prefill":
+        case = cases["prefill"]
+        flops, byt = prefill_work(case)
+        wall, ev = run_prefill(case, steps, warmup, torch, rba)
+        tf = flops / (ev * 1e-3) / 1e12
+        res = {"workload": name, "metric": "prefill attn TFLOP/s", "value": round(tf, 2),
+               "unit": "TFLOP/s", "ms_per_step": round(wall, 4), "kernel_ms": round(ev, 4),
+               "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+               "hbm_gbs": round(byt / (ev * 1e-3) / 1e9, 1)}
+    else:
+        splits = w.get("num_splits", 0)
+        flops = byt = 0
+        for c in cases.values():
+            f, b = decode_work(c)
+            flops += f
+            byt += b
+        wall, ev = run_decode(cases, splits, steps, warmup, torch, rba)
+        gbs = byt / (ev * 1e-3) / 1e9
+        res = {"workload": name, "metric": "decode KV-read GB/s", "value": round(gbs, 1),
+               "unit": "GB/s", "ms_per_step": round(wall, 4), "step_event_ms": round(ev, 4),
+               "algorithmic_bytes": byt,
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+               "splits": {k: rba.decode_num_splits(c.q, c.k_pool, c.v_pool, c.block_table,
+                                                   c.seq_lens_dev, c.max_seq_len, c.bias,
+                                                   window=c.spec.window, sm_scale=c.spec.scale(),
+                                                   num_splits=splits)
+                          for k, c in cases.items()}}
+    del cases
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=MAIN)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the cpu_baseline sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
+              "kernels shard by sequence and KV head with no exchange, so a multi-GPU figure "
+              "is the one-GPU figure times N and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rba_inputs as ri
+    import relative_position_bias_paged_amd as rba
+
+    rba.load()
+    dev = torch.device("cuda:0")
+    w = ri.WORKLOADS[args.workload]
+    if w["kind"] != "prefill":
+        raise SystemExit("the headline line is a prefill workload; decode runs under secondary")
+    case = ri.build_workload(args.workload, dev)["prefill"]
+    sp = case.spec
+    flops, byt = prefill_work(case)
+    wall, ev = run_prefill(case, args.steps, args.warmup, torch, rba)
+    tflops = flops / (wall * 1e-3) / 1e12
+    achieved = byt / (ev * 1e-3) / 1e9
+
+    result = {
+        "metric": "prefill attn TFLOP/s + decode KV-read GB/s (% MI355X peak), rel-bias paged",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v/bias, shuffled page placement)",
+        "config": {"workload": args.workload, "sequences": len(case.seq_lens),
+                   "seq_len": case.max_seqlen, "q_heads": sp.num_q_heads,
+                   "kv_heads": sp.num_kv_heads, "head_dim": sp.head_dim, "window": sp.window,
+                   "rel_extent": sp.rel_extent, "page_size": sp.page_size,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(args.workload, "prefill_bf16.hip"),
+                     "kernel": "prefill_bf16_kernel<128>", "kernel_ms": round(ev, 5),
+                     "algorithmic_bytes": byt, "algorithmic_flops": flops,
+                     "mfma_frac": round(flops / (ev * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    del case
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        result["secondary"] = [secondary(n, torch, rba, ri, steps=max(5, args.steps // 5),
+                                         warmup=2) for n in SECONDARY]
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

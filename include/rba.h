@@ -1,0 +1,191 @@
+/*
+ * rba.h -- C ABI of librba: paged attention with a learned relative-position
+ * bias, for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  For query position t of a sequence, query head
+ * h and every key position s of the same sequence,
+ *
+ *   score(t,s) = sm_scale * <q[t,h,:], k[s,g,:]> + bias[t,h,min(t-s, R-1)]
+ *   visible    = s <= t  and  (window <= 0  or  t - s < window)
+ *   out[t,h,:] = sum over visible s of softmax_s(score) * v[s,g,:]
+ *
+ * with g = h / (Hq / Hkv) and R = rel_extent.  Sources: TensorRT-LLM PR #17062
+ * "Support Inkling-NVFP4 model" -- Description, Architecture list (no RoPE;
+ * the position signal is a learned bias per (query token, head, relative
+ * distance) added before softmax; local layers use a causal sliding window,
+ * global layers are full causal), and its review comment on _build_rel_logits
+ * (the bias tensor is [T, heads, rel_extent]); TensorRT-LLM PR #17860 "Inkling
+ * attn backend cleanup fake registry" -- the commit making both Triton entry
+ * points assert num_heads % num_kv_heads (query head -> KV head is
+ * h // kv_group_num), and the commit borrowing the framework page table (keys
+ * are addressed as page = table[k_pos // page_size]; entries past a
+ * sequence's last page are never read because every access is bounded by
+ * k_pos < seq_len).
+ *
+ * General conventions (every entry point):
+ *  - All tensor pointers are DEVICE pointers to caller-owned memory.  The
+ *    library never allocates, frees or synchronises; work is enqueued on
+ *    `stream` (NULL = the null stream) and the call returns immediately.
+ *  - Host-side argument checks run before anything is enqueued; on any error
+ *    nothing is enqueued and the output is untouched.  Device contents (page
+ *    ids, sequence lengths) are never read by the host: keeping them in range
+ *    is the caller's contract (page ids in [0, num_pages) for every page
+ *    that holds a key below seq_len).
+ *  - Tensor pointers must be 16-byte aligned; all tensors are contiguous,
+ *    row-major in the shapes given.
+ *  - No C++ exception crosses the ABI.  The library holds no mutable global
+ *    state; calls on different streams may run concurrently.
+ */
+#ifndef RBA_H
+#define RBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rba_status {
+  RBA_OK = 0,
+  RBA_ERR_INVALID_ARG = 1, /* a null pointer, an inconsistent size, Hq % Hkv != 0,
+                              page_size not a power of two, rel_extent < 1, ... */
+  RBA_ERR_UNSUPPORTED = 2, /* valid, but not a shape/dtype this build runs
+                              (see each call) */
+  RBA_ERR_WORKSPACE = 3,   /* workspace null or smaller than required */
+  RBA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} rba_status;
+
+typedef enum rba_dtype {
+  RBA_BF16 = 0, /* q, k, v, bias and out in bfloat16 (fp32 accumulation) */
+  RBA_F32 = 1   /* q, k, v, bias and out in float32 */
+} rba_dtype;
+
+/*
+ * Page table.  Key position s of sequence b lives in pool page
+ * block_table[b * max_pages_per_seq + s / page_size], slot s % page_size.
+ * The table is positional: entry j always describes key positions
+ * j*page_size .. j*page_size + page_size - 1.  Entries at or past
+ * ceil(seq_lens[b] / page_size) are never read (0 by convention).
+ */
+typedef struct rba_page_table {
+  const int32_t *block_table; /* device, [num_seqs][max_pages_per_seq] */
+  const int32_t *seq_lens;    /* device, [num_seqs]: keys held per sequence;
+                                 decode: the current token's key included */
+  int32_t num_seqs;
+  int32_t max_pages_per_seq;
+  int32_t page_size;          /* power of two, 16 .. 1024 */
+  int32_t num_pages;          /* pool size in pages */
+} rba_page_table;
+
+/*
+ * Paged KV pool.  K and V are separate pools of identical shape
+ * [num_pages][num_kv_heads][page_size][head_dim]: inside one page, each KV
+ * head's page_size x head_dim block is contiguous.
+ */
+typedef struct rba_kv_cache {
+  const void *k_pool;
+  const void *v_pool;
+  int32_t num_kv_heads;
+  int32_t head_dim;           /* bf16: 64 or 128; f32: 64 or 128 */
+  rba_dtype dtype;            /* also the dtype of q, bias and out */
+} rba_kv_cache;
+
+/*
+ * Per-layer scalars (the three the pages name: sm_scale, rel_extent and the
+ * window, with window <= 0 meaning full causal like window_left = -1).
+ */
+typedef struct rba_attn_params {
+  int32_t num_q_heads;        /* Hq, a multiple of num_kv_heads */
+  int32_t window;             /* > 0: key visible iff 0 <= t - s < window;
+                                 <= 0: full causal */
+  int32_t rel_extent;         /* R >= 1: buckets per bias row; distances
+                                 >= R-1 share bucket R-1 */
+  float sm_scale;             /* > 0, finite; multiplies q.k, not the bias */
+} rba_attn_params;
+
+/*
+ * Prefill: every token of every sequence is a query; the keys of sequence b
+ * are its own tokens (positions 0 .. L_b - 1), already written to the pool.
+ *
+ *  q           [total_tokens][Hq][head_dim]; sequence b owns tokens
+ *              cu_seqlens[b] .. cu_seqlens[b+1]-1, token cu_seqlens[b]+t
+ *              being position t
+ *  cu_seqlens  device int32 [num_seqs + 1], non-decreasing, cu[0] = 0,
+ *              cu[num_seqs] = total_tokens; L_b must equal pt->seq_lens[b]
+ *  max_seqlen  host bound on max_b L_b (sizes the grid)
+ *  bias        [total_tokens][Hq][rel_extent]
+ *  out         [total_tokens][Hq][head_dim] (written)
+ *  lse         NULL or float [total_tokens][Hq]: natural-log sum of
+ *              exp(score) over the visible keys (written)
+ *
+ * RBA_ERR_INVALID_ARG if a pointer is null or misaligned, a count is
+ * negative, Hq % Hkv != 0, page_size is not a power of two, rel_extent < 1,
+ * sm_scale is not finite and positive, or max_seqlen exceeds
+ * max_pages_per_seq * page_size.  RBA_ERR_UNSUPPORTED for a head_dim or
+ * page_size outside the ranges above.  total_tokens == 0 or num_seqs == 0
+ * is a no-op returning RBA_OK.
+ */
+rba_status rba_prefill(const void *q, const int32_t *cu_seqlens,
+                       int32_t total_tokens, int32_t max_seqlen,
+                       const rba_kv_cache *kv, const rba_page_table *pt,
+                       const void *bias, const rba_attn_params *params,
+                       void *out, float *lse, hipStream_t stream);
+
+/*
+ * Number of key-range partitions rba_decode will use for these arguments
+ * (num_splits == 0 picks one from the host bound max_seq_len; otherwise the
+ * requested count, capped at 256).  Returns 0 on invalid arguments.
+ */
+int32_t rba_decode_num_splits(const rba_kv_cache *kv, const rba_page_table *pt,
+                              int32_t max_seq_len,
+                              const rba_attn_params *params,
+                              int32_t num_splits);
+
+/*
+ * Bytes of device workspace rba_decode needs for these arguments (0 when it
+ * runs without partitions).  Returns 0 on invalid arguments as well.
+ */
+size_t rba_decode_workspace_size(const rba_kv_cache *kv,
+                                 const rba_page_table *pt, int32_t max_seq_len,
+                                 const rba_attn_params *params,
+                                 int32_t num_splits);
+
+/*
+ * Single-token decode: one query per sequence at position seq_lens[b] - 1,
+ * attending the seq_lens[b] keys in the pool (its own key included).  With
+ * more than one partition the visible key range of each sequence is cut into
+ * page-aligned partitions, each partition's normalised partial output and
+ * log-sum-exp go to the workspace, and a second kernel merges them with
+ * weights exp(lse_j - max_j lse_j).
+ *
+ *  q           [num_seqs][Hq][head_dim]
+ *  max_seq_len host bound on max_b seq_lens[b] (sizes the grid)
+ *  bias        [num_seqs][Hq][rel_extent]: the bias row of each query
+ *  num_splits  0 = automatic, else the partition count (capped at 256)
+ *  workspace   device memory of rba_decode_workspace_size() bytes, 256-byte
+ *              aligned (may be NULL when that size is 0); contents on entry
+ *              are ignored
+ *  out         [num_seqs][Hq][head_dim] (written)
+ *  lse         NULL or float [num_seqs][Hq] (written)
+ *
+ * Errors as for rba_prefill, plus RBA_ERR_WORKSPACE.  A sequence with
+ * seq_lens[b] == 0 gets a zero output row and lse = -inf.
+ */
+rba_status rba_decode(const void *q, const rba_kv_cache *kv,
+                      const rba_page_table *pt, int32_t max_seq_len,
+                      const void *bias, const rba_attn_params *params,
+                      int32_t num_splits, void *workspace,
+                      size_t workspace_bytes, void *out, float *lse,
+                      hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char *rba_status_string(rba_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RBA_H */

@@ -1,0 +1,253 @@
+"""Python binding of librba: paged attention with a learned relative-position
+bias on AMD Instinct MI355X (gfx950).
+
+This module only marshals arguments: it checks tensor placement, dtypes and
+shapes, turns them into the C structs of ``include/rba.h`` and calls the
+library on the current HIP stream.  Every step of the computation runs in the
+HIP kernels of ``librba.so``; there is no fallback.  If the library has not
+been built (``__graft_entry__.build()`` or ``python -m
+relative_position_bias_paged_amd.build``) any call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_size",
+           "status_string", "RbaError", "library_path", "load"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librba.so")
+
+RBA_OK = 0
+RBA_ERR_INVALID_ARG = 1
+RBA_ERR_UNSUPPORTED = 2
+RBA_ERR_WORKSPACE = 3
+RBA_ERR_HIP = 4
+
+RBA_BF16 = 0
+RBA_F32 = 1
+
+# every symbol include/rba.h declares
+EXPORTED = ("rba_prefill", "rba_decode", "rba_decode_num_splits",
+            "rba_decode_workspace_size", "rba_status_string")
+
+
+class rba_page_table(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p),
+                ("num_seqs", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32),
+                ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
+
+
+class rba_kv_cache(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p),
+                ("v_pool", ctypes.c_void_p),
+                ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int)]
+
+
+class rba_attn_params(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32),
+                ("window", ctypes.c_int32),
+                ("rel_extent", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class RbaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load librba.so (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+            "(hipcc --offload-arch=gfx950); there is no fallback implementation")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER
+    lib.rba_prefill.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                P(rba_kv_cache), P(rba_page_table), ctypes.c_void_p,
+                                P(rba_attn_params), ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    lib.rba_prefill.restype = ctypes.c_int
+    lib.rba_decode.argtypes = [ctypes.c_void_p, P(rba_kv_cache), P(rba_page_table), ctypes.c_int32,
+                               ctypes.c_void_p, P(rba_attn_params), ctypes.c_int32,
+                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.rba_decode.restype = ctypes.c_int
+    lib.rba_decode_num_splits.argtypes = [P(rba_kv_cache), P(rba_page_table), ctypes.c_int32,
+                                          P(rba_attn_params), ctypes.c_int32]
+    lib.rba_decode_num_splits.restype = ctypes.c_int32
+    lib.rba_decode_workspace_size.argtypes = [P(rba_kv_cache), P(rba_page_table), ctypes.c_int32,
+                                              P(rba_attn_params), ctypes.c_int32]
+    lib.rba_decode_workspace_size.restype = ctypes.c_size_t
+    lib.rba_status_string.argtypes = [ctypes.c_int]
+    lib.rba_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().rba_status_string(int(status)).decode()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+
+_DTYPES = {torch.bfloat16: RBA_BF16, torch.float32: RBA_F32}
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _structs(k_pool, v_pool, block_table, seq_lens, num_q_heads, window, rel_extent, sm_scale):
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool must both be [num_pages, Hkv, page_size, head_dim]")
+    if k_pool.dtype not in _DTYPES or v_pool.dtype != k_pool.dtype:
+        raise TypeError("k_pool / v_pool must be bf16 or fp32 and match")
+    num_pages, hkv, page, hd = k_pool.shape
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, max_pages_per_seq]")
+    kv = rba_kv_cache(_dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), hkv, hd, _DTYPES[k_pool.dtype])
+    pt = rba_page_table(_dev(block_table, "block_table", torch.int32),
+                        _dev(seq_lens, "seq_lens", torch.int32) if seq_lens is not None else None,
+                        block_table.shape[0], block_table.shape[1], page, num_pages)
+    prm = rba_attn_params(int(num_q_heads), int(window), int(rel_extent), float(sm_scale))
+    return kv, pt, prm
+
+
+def _check(status: int, where: str):
+    if status != RBA_OK:
+        raise RbaError(status, where)
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the rba_ prefix)
+
+def prefill(q: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+            k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+            seq_lens: Optional[torch.Tensor], bias: torch.Tensor, *, window: int,
+            sm_scale: float, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rba_prefill: q [T,Hq,D], bias [T,Hq,R], pools [pages,Hkv,P,D]; returns out [T,Hq,D]."""
+    lib = load()
+    if q.dim() != 3 or bias.dim() != 3 or bias.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [T,Hq,D] and bias [T,Hq,R]")
+    T, hq, hd = q.shape
+    kv, pt, prm = _structs(k_pool, v_pool, block_table, seq_lens, hq, window, bias.shape[2], sm_scale)
+    if q.dtype != k_pool.dtype or bias.dtype != k_pool.dtype:
+        raise TypeError("q, bias and the pools must share one dtype")
+    if hd != k_pool.shape[3]:
+        raise ValueError("head_dim of q and pools differ")
+    if cu_seqlens.numel() != block_table.shape[0] + 1:
+        raise ValueError("cu_seqlens must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lse_ptr = None
+    if lse is not None:
+        if lse.shape != (T, hq):
+            raise ValueError("lse must be [T, Hq]")
+        lse_ptr = _dev(lse, "lse", torch.float32)
+    st = lib.rba_prefill(_dev(q, "q"), _dev(cu_seqlens, "cu_seqlens", torch.int32), T,
+                         int(max_seqlen), ctypes.byref(kv), ctypes.byref(pt),
+                         _dev(bias, "bias"), ctypes.byref(prm), _dev(out, "out"), lse_ptr,
+                         _stream(stream))
+    _check(st, "rba_prefill")
+    return out
+
+
+def _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale):
+    if q.dim() != 3 or bias.dim() != 3 or bias.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [B,Hq,D] and bias [B,Hq,R]")
+    return _structs(k_pool, v_pool, block_table, seq_lens, q.shape[1], window,
+                    bias.shape[2], sm_scale)
+
+
+def decode_num_splits(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, bias, *,
+                      window: int, sm_scale: float, num_splits: int = 0) -> int:
+    lib = load()
+    kv, pt, prm = _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale)
+    return int(lib.rba_decode_num_splits(ctypes.byref(kv), ctypes.byref(pt), int(max_seq_len),
+                                         ctypes.byref(prm), int(num_splits)))
+
+
+def decode_workspace_size(q, k_pool, v_pool, block_table, seq_lens, max_seq_len, bias, *,
+                          window: int, sm_scale: float, num_splits: int = 0) -> int:
+    lib = load()
+    kv, pt, prm = _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale)
+    return int(lib.rba_decode_workspace_size(ctypes.byref(kv), ctypes.byref(pt), int(max_seq_len),
+                                             ctypes.byref(prm), int(num_splits)))
+
+
+def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+           block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+           bias: torch.Tensor, *, window: int, sm_scale: float, num_splits: int = 0,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rba_decode: q [B,Hq,D], bias [B,Hq,R]; returns out [B,Hq,D].
+
+    ``workspace`` (a uint8 device tensor) is allocated with torch when not
+    given and the call needs one.
+    """
+    lib = load()
+    kv, pt, prm = _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale)
+    if q.dtype != k_pool.dtype or bias.dtype != k_pool.dtype:
+        raise TypeError("q, bias and the pools must share one dtype")
+    need = int(lib.rba_decode_workspace_size(ctypes.byref(kv), ctypes.byref(pt), int(max_seq_len),
+                                             ctypes.byref(prm), int(num_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lse_ptr = None
+    if lse is not None:
+        if lse.shape != q.shape[:2]:
+            raise ValueError("lse must be [B, Hq]")
+        lse_ptr = _dev(lse, "lse", torch.float32)
+    st = lib.rba_decode(_dev(q, "q"), ctypes.byref(kv), ctypes.byref(pt), int(max_seq_len),
+                        _dev(bias, "bias"), ctypes.byref(prm), int(num_splits), ws_ptr, ws_bytes,
+                        _dev(out, "out"), lse_ptr, _stream(stream))
+    _check(st, "rba_decode")
+    return out

@@ -1,0 +1,78 @@
+"""Build librba.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+The library is built in-tree, next to this file, so that it travels with the
+source tree.  Every HIP source is compiled with packed-fp32 instruction
+selection disabled (those forms are avoided on this hardware) and the host
+symbols are hidden except the rba_* entry points.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "librba.so")
+
+SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "rba_api.cpp"]
+ARCH = os.environ.get("RBA_OFFLOAD_ARCH", "gfx950")
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source to an object, then link librba.so.  Returns its path."""
+    cc = hipcc()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    common = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+              "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        objs.append(obj)
+        cmd = [cc, *common, "-x", "hip", f"--offload-arch={ARCH}",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0))
+    for p in procs:
+        _wait(p)
+    tmp = LIB + ".tmp"
+    link = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _wait(item):
+    src, proc = item
+    out, _ = proc.communicate()
+    text = out.decode(errors="replace")
+    # the host pass does not know the packed-fp32 feature name; that note is harmless
+    lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
+    if proc.returncode != 0:
+        raise RuntimeError(f"compile of {src} failed:\n" + "\n".join(lines))
+    if lines:
+        print(f"[{src}]\n" + "\n".join(lines), file=sys.stderr)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

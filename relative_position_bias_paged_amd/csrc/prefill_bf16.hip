@@ -1,0 +1,419 @@
+// prefill_bf16.hip -- prefill attention with a learned relative-position bias
+// over a paged KV pool, bf16 in / fp32 accumulate, for gfx950 (CDNA4).
+//
+// Computes, for every query token t of a sequence and query head h,
+//   out[t,h] = softmax_s( sm_scale * q[t,h].k[s,g] + bias[t,h,min(t-s,R-1)] ) v[s,g]
+// over the visible keys s (s <= t, and t - s < window on local layers),
+// g = h / (Hq/Hkv).  The bias is added before the softmax and indexed by
+// (query token, head, relative distance) as the TensorRT-LLM PR #17062 page
+// ("Support Inkling-NVFP4 model", Description, Architecture list) states;
+// its [T, heads, rel_extent] shape is the one in that page's review comment
+// on _build_rel_logits.
+//
+// Work decomposition (one work-group = 4 waves = 128 queries of one head):
+//  * a 64-key K tile and the transposed V tile are staged through LDS,
+//    prefetched into registers one tile ahead;
+//  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16, so each
+//    lane owns one query column: the softmax row statistics stay in a lane
+//    pair (lane, lane^32);
+//  * the bias of query row t at distance d sits in a per-row ring of two
+//    64-wide distance chunks in LDS (element d at d mod 128); each key tile
+//    brings in one new chunk per row, loaded with aligned 16-byte reads, so
+//    every bias element crosses HBM once.  Tiles whose distances all lie at
+//    or beyond R-1 use the single clamped value bias[t,h,R-1] instead;
+//  * masking selects (never multiplies), so NaN in keys past the end of a
+//    sequence or in masked positions cannot leak into the output;
+//  * the running max is rescaled lazily (only when a row's max grows by more
+//    than 2^8), which is exact because numerator and denominator share it.
+#include "rba_internal.h"
+
+namespace rba {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BM = 128;        // queries per work-group
+constexpr int BN = 64;         // keys per tile (= one bias chunk)
+constexpr int NTHREADS = 256;
+constexpr int RING = 128;      // bias ring elements per query row
+constexpr int VT_STRIDE = BN + 4;  // V^T row: 34 dwords, conflict-free 8-byte reads
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float NEG_INIT = -1.0e30f;  // finite start of the running max (log2 units)
+constexpr float TAU = 8.0f;           // lazy-rescale threshold (log2 units)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo);
+  __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <int D>
+struct __align__(16) PrefillSmem {
+  uint16_t k[BN * D];           // K tile, 16-byte chunks XOR-swizzled by key
+  uint16_t vt[D * VT_STRIDE];   // V^T tile
+  uint16_t ring[BM * RING];     // bias ring
+};
+
+template <int D>
+__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
+  constexpr int KPT = BN * CHUNKS / NTHREADS;   // key rows per thread per tile
+  constexpr int KB = D / 16;                    // MFMA k-steps over head_dim
+  constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
+  __shared__ PrefillSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // Work-group -> (sequence, head, query tile).  Blocks are dealt to the 8
+  // XCDs round-robin; remap so each XCD walks a contiguous range, in which
+  // the query heads of one KV head and its query tiles (heaviest first)
+  // are adjacent and share that XCD's L2.
+  const int nb = a.num_blocks;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, xidx = bid >> 3;
+  const int base = nb >> 3, rem = nb & 7;
+  const int r = (xcd < rem) ? xcd * (base + 1) + xidx
+                            : rem * (base + 1) + (xcd - rem) * base + xidx;
+  const int nqt = a.num_qtiles;
+  const int per_seq = a.Hq * nqt;
+  const int b = r / per_seq;
+  int rr = r - b * per_seq;
+  const int per_kvh = a.G * nqt;
+  const int kvh = rr / per_kvh;
+  rr -= kvh * per_kvh;
+  const int qt = nqt - 1 - rr / a.G;
+  const int h = kvh * a.G + rr % a.G;
+
+  const int tok0 = a.cu_seqlens[b];
+  const int L = a.cu_seqlens[b + 1] - tok0;
+  const int t0 = qt * BM;
+  if (t0 >= L) return;
+
+  const int Hq = a.Hq;
+  const int R = a.R;
+  const int W = a.window;
+  const int t_last = min(t0 + BM, L) - 1;
+  int s_begin = (W > 0) ? max(0, t0 - W + 1) : 0;
+  s_begin &= ~(BN - 1);
+
+  const uint16_t *qp = static_cast<const uint16_t *>(a.q);
+  const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
+  const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
+  const uint16_t *bp = static_cast<const uint16_t *>(a.bias);
+  const int32_t *trow = a.block_table + (size_t)b * a.max_pages;
+  const int P = a.page_size;
+  const int lp = a.log2_page;
+  const size_t head_stride = (size_t)P * D;           // elements per (page, head)
+  const size_t page_stride = (size_t)a.Hkv * head_stride;
+
+  // ---- this lane's query row --------------------------------------------
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int q_local = wave * 32 + col;
+  const int t = t0 + q_local;
+  const bool row_ok = t < L;
+  const size_t row = ((size_t)tok0 + (row_ok ? t : 0)) * Hq + h;
+
+  u32x4_t qf[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    qf[kb] = row_ok ? *reinterpret_cast<const u32x4_t *>(qp + row * D + kb * 16 + half * 8)
+                    : u32x4_t{0, 0, 0, 0};
+  }
+  const float b_last = row_ok ? bf16_to_f32(bp[row * R + (R - 1)]) : 0.f;
+
+  // ---- K/V tile loaders ----------------------------------------------------
+  const int kc = tid % CHUNKS;          // 16-byte chunk this thread moves
+  const int krow0 = tid / CHUNKS;       // K rows krow0 + j*(NTHREADS/CHUNKS)
+  const int vkey0 = (tid / CHUNKS) * KPT;  // V keys vkey0 .. vkey0+KPT-1
+
+  u32x4_t kreg[KPT], vreg[KPT];
+
+  auto kv_offset = [&](int s) -> size_t {  // element offset of key s, chunk kc
+    const int page = trow[s >> lp];
+    return (size_t)page * page_stride + (size_t)kvh * head_stride +
+           (size_t)(s & (P - 1)) * D + kc * 8;
+  };
+
+  auto load_kv = [&](int s0) {
+    if (P >= BN) {
+      const int page = trow[s0 >> lp];
+      const size_t pb = (size_t)page * page_stride + (size_t)kvh * head_stride +
+                        (size_t)(s0 & (P - 1)) * D + kc * 8;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int kr = krow0 + j * (NTHREADS / CHUNKS);
+        kreg[j] = (s0 + kr < L) ? *reinterpret_cast<const u32x4_t *>(kp + pb + (size_t)kr * D)
+                                : u32x4_t{0, 0, 0, 0};
+        const int vk = vkey0 + j;
+        vreg[j] = (s0 + vk < L) ? *reinterpret_cast<const u32x4_t *>(vp + pb + (size_t)vk * D)
+                                : u32x4_t{0, 0, 0, 0};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int kr = krow0 + j * (NTHREADS / CHUNKS);
+        kreg[j] = (s0 + kr < L) ? *reinterpret_cast<const u32x4_t *>(kp + kv_offset(s0 + kr))
+                                : u32x4_t{0, 0, 0, 0};
+        const int vk = vkey0 + j;
+        vreg[j] = (s0 + vk < L) ? *reinterpret_cast<const u32x4_t *>(vp + kv_offset(s0 + vk))
+                                : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto commit_kv = [&]() {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int kr = krow0 + j * (NTHREADS / CHUNKS);
+      const int phys = kc ^ (kr & (CHUNKS - 1));
+      *reinterpret_cast<u32x4_t *>(&sm.k[kr * D + phys * 8]) = kreg[j];
+    }
+    // V^T: element (key, d) -> vt[d][key]; this thread holds keys
+    // vkey0..vkey0+KPT-1 of head-dim chunk kc.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const int d = kc * 8 + e;
+      if constexpr (KPT == 4) {
+        u32x2_t pk;
+        pk[0] = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
+        pk[1] = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2_t *>(&sm.vt[d * VT_STRIDE + vkey0]) = pk;
+      } else {
+        const uint32_t pk = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<uint32_t *>(&sm.vt[d * VT_STRIDE + vkey0]) = pk;
+      }
+    }
+  };
+
+  // ---- bias ring loader: one 64-wide distance chunk per query row ----------
+  // For key tile s0, row q needs distances t0+q-s0-63 .. t0+q-s0, i.e. the
+  // chunks lo(q) = floor((t0-s0-63+q)/64) and lo(q)+1.  Moving to the next
+  // tile (s0 += 64) needs chunk lo-1 and drops lo+1: same ring slot.
+  u32x4_t breg[4];
+  const bool r_vec = (R & 7) == 0;
+
+  auto chunk_of = [&](int s0, int q, int which) { return ((t0 - s0 - (BN - 1) + q) >> 6) + which; };
+
+  auto load_chunk = [&](int s0, int which) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = tid + j * NTHREADS;
+      const int q = u >> 3, v = u & 7;
+      const int e = chunk_of(s0, q, which) * BN + v * 8;
+      const bool ok = (t0 + q < L) && e >= 0 && e < R;
+      u32x4_t val = {0, 0, 0, 0};
+      if (ok) {
+        const uint16_t *src = bp + ((size_t)tok0 + t0 + q) * Hq * R + (size_t)h * R + e;
+        if (r_vec) {
+          val = *reinterpret_cast<const u32x4_t *>(src);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const uint32_t el = (e + x < R) ? (uint32_t)src[x] : 0u;
+            val[x >> 1] |= el << ((x & 1) * 16);
+          }
+        }
+      }
+      breg[j] = val;
+    }
+  };
+
+  auto commit_chunk = [&](int s0, int which) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = tid + j * NTHREADS;
+      const int q = u >> 3, v = u & 7;
+      const int e = chunk_of(s0, q, which) * BN + v * 8;
+      if ((t0 + q < L) && e >= 0 && e < R)
+        *reinterpret_cast<u32x4_t *>(&sm.ring[q * RING + (e & (RING - 1))]) = breg[j];
+    }
+  };
+
+  // ---- accumulators ------------------------------------------------------
+  f32x16_t oacc[DSUB];
+#pragma unroll
+  for (int i = 0; i < DSUB; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
+  float m2 = NEG_INIT;   // running max, log2 units, shared by the lane pair
+  float lsum = 0.f;      // this lane's share of the softmax denominator
+  const float scale = a.sm_scale;
+
+  auto compute_tile = [&](int s0) {
+    const int tq0 = t0 + wave * 32;
+    const int dmax_w = tq0 + 31 - s0;
+    const int dmin_w = tq0 - (s0 + BN - 1);
+    if (dmax_w < 0) return;                    // every key lies in this wave's future
+    if (W > 0 && dmin_w >= W) return;          // every key lies before the window
+    const bool need_mask = (dmin_w < 0) || (W > 0 && dmax_w >= W) || (s0 + BN > L);
+    const bool band = dmin_w < R - 1;
+
+    // S^T = K Q^T : two 32x32 blocks of keys x queries
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sacc[sub][j] = 0.f;
+      const int key_row = sub * 32 + col;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int phys = (2 * kb + half) ^ (key_row & (CHUNKS - 1));
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(&sm.k[key_row * D + phys * 8]);
+        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, kf), __builtin_bit_cast(bf16x8_t, qf[kb]), sacc[sub], 0, 0, 0);
+      }
+    }
+
+    // scores: scale, bias, mask
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = s0 + sub * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        const int d = t - key;
+        float bv = b_last;
+        if (band) {
+          const float ringv = bf16_to_f32(sm.ring[q_local * RING + (d & (RING - 1))]);
+          bv = (d < R - 1) ? ringv : b_last;
+        }
+        float x = fmaf(sacc[sub][j], scale, bv);
+        if (need_mask) {
+          const bool vis = (d >= 0) && (W <= 0 || d < W) && (key < L);
+          x = vis ? x : -INFINITY;
+        }
+        sacc[sub][j] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+    // online softmax with lazy rescaling
+    const float mt2 = mx * LOG2E;
+    const bool exceed = mt2 > m2 + TAU;
+    if (__ballot(exceed)) {
+      const float mnew = exceed ? mt2 : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DSUB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
+      m2 = mnew;
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sub][j], LOG2E, -m2));
+        lsum += p;
+        sacc[sub][j] = p;
+      }
+
+    // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` are keys
+    // ks*16 + 4*half + {0,1,2,3,8,9,10,11}: exactly S^T registers 8*(ks&1)+0..7.
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+      const int sub = ks >> 1, rb = (ks & 1) * 8;
+      u32x4_t pw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(sacc[sub][rb + 2 * j], sacc[sub][rb + 2 * j + 1]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+      for (int ds = 0; ds < DSUB; ++ds) {
+        const int drow = ds * 32 + col;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(&sm.vt[drow * VT_STRIDE + ks * 16 + 4 * half]);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(&sm.vt[drow * VT_STRIDE + ks * 16 + 8 + 4 * half]);
+        const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pb, oacc[ds], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop: prefetch tile i+1 while computing tile i -----------------
+  auto wg_band = [&](int s0) { return t0 - (s0 + BN - 1) < R - 1; };
+
+  load_kv(s_begin);
+  bool ring_ready = false;
+  const bool band0 = wg_band(s_begin);
+  if (band0) load_chunk(s_begin, 0);
+  commit_kv();
+  if (band0) {
+    commit_chunk(s_begin, 0);
+    load_chunk(s_begin, 1);
+    commit_chunk(s_begin, 1);
+    ring_ready = true;
+  }
+  __syncthreads();
+
+  for (int s0 = s_begin; s0 <= t_last; s0 += BN) {
+    const int sn = s0 + BN;
+    const bool has_next = sn <= t_last;
+    const bool band_next = has_next && wg_band(sn);
+    if (has_next) {
+      load_kv(sn);
+      if (band_next) load_chunk(sn, 0);
+    }
+    compute_tile(s0);
+    __syncthreads();
+    if (has_next) {
+      commit_kv();
+      if (band_next) {
+        commit_chunk(sn, 0);
+        if (!ring_ready) {
+          load_chunk(sn, 1);
+          commit_chunk(sn, 1);
+          ring_ready = true;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue ------------------------------------------------------------
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (row_ok) {
+    const float inv = 1.0f / ltot;
+    uint16_t *op = static_cast<uint16_t *>(a.out) + row * D;
+#pragma unroll
+    for (int ds = 0; ds < DSUB; ++ds)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = ds * 32 + 8 * g + 4 * half;
+        u32x2_t w;
+        w[0] = pack_bf16x2(oacc[ds][4 * g + 0] * inv, oacc[ds][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(oacc[ds][4 * g + 2] * inv, oacc[ds][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2_t *>(op + d0) = w;
+      }
+    if (a.lse != nullptr && half == 0) a.lse[row] = (m2 + __log2f(ltot)) * LN2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
+  dim3 grid(a.num_blocks), block(NTHREADS);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, s, a);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rba

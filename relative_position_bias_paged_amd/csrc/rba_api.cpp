@@ -1,0 +1,252 @@
+// rba_api.cpp -- host entry points of librba (declared in include/rba.h).
+//
+// Every call validates its host-side arguments, sizes the launch from host
+// scalars only (never reading device memory, so calls can be enqueued from
+// any context, including graph capture), and enqueues the kernels on the
+// caller's stream.  Nothing here allocates, frees or synchronises.
+#include "rba.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "rba_internal.h"
+
+#define RBA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kPrefillBM = 128;      // queries per bf16 prefill work-group
+constexpr int kF32Rows = 64;         // queries per fp32 prefill work-group
+constexpr int kMaxSplits = 256;
+constexpr int kAutoChunkPages = 32;  // automatic partitions hold about this many pages
+constexpr long long kAutoMinWaves = 2048;
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+rba_status check_layer(const rba_kv_cache *kv, const rba_page_table *pt,
+                       const rba_attn_params *p) {
+  if (kv == nullptr || pt == nullptr || p == nullptr) return RBA_ERR_INVALID_ARG;
+  if (kv->dtype != RBA_BF16 && kv->dtype != RBA_F32) return RBA_ERR_INVALID_ARG;
+  if (kv->num_kv_heads <= 0 || p->num_q_heads <= 0) return RBA_ERR_INVALID_ARG;
+  if (p->num_q_heads % kv->num_kv_heads != 0) return RBA_ERR_INVALID_ARG;
+  if (kv->head_dim <= 0) return RBA_ERR_INVALID_ARG;
+  if (!is_pow2(pt->page_size)) return RBA_ERR_INVALID_ARG;
+  if (p->rel_extent < 1) return RBA_ERR_INVALID_ARG;
+  if (!(p->sm_scale > 0.0f) || !std::isfinite(p->sm_scale)) return RBA_ERR_INVALID_ARG;
+  if (pt->num_seqs < 0 || pt->max_pages_per_seq < 0 || pt->num_pages < 0)
+    return RBA_ERR_INVALID_ARG;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return RBA_ERR_UNSUPPORTED;
+  if (pt->page_size < 16 || pt->page_size > 1024) return RBA_ERR_UNSUPPORTED;
+  return RBA_OK;
+}
+
+bool pool_ok(const rba_kv_cache *kv, const rba_page_table *pt) {
+  return kv->k_pool != nullptr && kv->v_pool != nullptr && pt->block_table != nullptr &&
+         aligned16(kv->k_pool) && aligned16(kv->v_pool) && pt->num_pages > 0 &&
+         pt->max_pages_per_seq > 0;
+}
+
+// Upper bound on the pages one decode row touches: the visible keys
+// [max(0, n - window), n) span at most ceil(visible / P) pages, plus one when
+// a window start falls inside a page.
+int decode_pages_max(const rba_page_table *pt, int max_seq_len, int window) {
+  const long long P = pt->page_size;
+  long long visible = max_seq_len;
+  if (window > 0 && window < visible) visible = window;
+  long long pages = (visible + P - 1) / P + (window > 0 ? 1 : 0);
+  if (pages < 1) pages = 1;
+  const long long cap = (max_seq_len + P - 1) / P;
+  if (pages > cap && cap > 0) pages = cap;
+  return (int)pages;
+}
+
+struct SplitPlan {
+  int splits;
+  int chunk_pages;
+};
+
+SplitPlan plan_splits(const rba_kv_cache *kv, const rba_page_table *pt, int max_seq_len,
+                      const rba_attn_params *p, int num_splits) {
+  if (kv->dtype == RBA_F32) return {1, 1 << 30};
+  const int pm = decode_pages_max(pt, max_seq_len, p->window);
+  int s;
+  if (num_splits > 0) {
+    s = num_splits;
+  } else {
+    s = (pm + kAutoChunkPages - 1) / kAutoChunkPages;
+    const int G = p->num_q_heads / kv->num_kv_heads;
+    const long long base = (long long)pt->num_seqs * kv->num_kv_heads * ((G + 3) / 4);
+    if (base > 0 && base * s < kAutoMinWaves) s = (int)((kAutoMinWaves + base - 1) / base);
+  }
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > pm) s = pm;
+  if (s < 1) s = 1;
+  const int chunk = (pm + s - 1) / s;
+  s = (pm + chunk - 1) / chunk;  // drop partitions that could never hold a page
+  return {s, chunk};
+}
+
+size_t workspace_bytes_for(const rba_kv_cache *kv, const rba_page_table *pt,
+                           const rba_attn_params *p, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)pt->num_seqs * p->num_q_heads;
+  const size_t o_bytes = rows * splits * kv->head_dim * sizeof(float);
+  const size_t o_padded = (o_bytes + 255) & ~(size_t)255;
+  return o_padded + rows * splits * sizeof(float);
+}
+
+}  // namespace
+
+RBA_EXPORT const char *rba_status_string(rba_status status) {
+  switch (status) {
+    case RBA_OK: return "RBA_OK";
+    case RBA_ERR_INVALID_ARG: return "RBA_ERR_INVALID_ARG";
+    case RBA_ERR_UNSUPPORTED: return "RBA_ERR_UNSUPPORTED";
+    case RBA_ERR_WORKSPACE: return "RBA_ERR_WORKSPACE";
+    case RBA_ERR_HIP: return "RBA_ERR_HIP";
+  }
+  return "RBA_UNKNOWN_STATUS";
+}
+
+RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int32_t total_tokens,
+                                  int32_t max_seqlen, const rba_kv_cache *kv,
+                                  const rba_page_table *pt, const void *bias,
+                                  const rba_attn_params *params, void *out, float *lse,
+                                  hipStream_t stream) {
+  rba_status st = check_layer(kv, pt, params);
+  if (st != RBA_OK) return st;
+  if (total_tokens < 0 || max_seqlen < 0) return RBA_ERR_INVALID_ARG;
+  if (total_tokens == 0 || pt->num_seqs == 0 || max_seqlen == 0) return RBA_OK;
+  if (q == nullptr || cu_seqlens == nullptr || bias == nullptr || out == nullptr)
+    return RBA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(bias) || !aligned16(out) || !pool_ok(kv, pt))
+    return RBA_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
+  if ((long long)max_seqlen > (long long)pt->max_pages_per_seq * pt->page_size)
+    return RBA_ERR_INVALID_ARG;
+
+  rba::PrefillArgs a{};
+  a.q = q;
+  a.cu_seqlens = cu_seqlens;
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = pt->block_table;
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.num_seqs = pt->num_seqs;
+  a.Hq = params->num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.max_pages = pt->max_pages_per_seq;
+  a.page_size = pt->page_size;
+  a.log2_page = ilog2(pt->page_size);
+  a.window = params->window > 0 ? params->window : 0;
+  a.R = params->rel_extent;
+  a.sm_scale = params->sm_scale;
+
+  hipError_t err;
+  if (kv->dtype == RBA_BF16) {
+    a.num_qtiles = (max_seqlen + kPrefillBM - 1) / kPrefillBM;
+    const long long blocks = (long long)a.num_seqs * a.Hq * a.num_qtiles;
+    if (blocks > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
+    a.num_blocks = (int32_t)blocks;
+    err = rba::launch_prefill_bf16(a, kv->head_dim, stream);
+  } else {
+    a.num_qtiles = (max_seqlen + kF32Rows - 1) / kF32Rows;
+    if (a.Hq > 65535 || a.num_seqs > 65535) return RBA_ERR_UNSUPPORTED;
+    a.num_blocks = a.num_qtiles;
+    err = rba::launch_prefill_f32(a, kv->head_dim, stream);
+  }
+  return err == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}
+
+RBA_EXPORT int32_t rba_decode_num_splits(const rba_kv_cache *kv, const rba_page_table *pt,
+                                         int32_t max_seq_len, const rba_attn_params *params,
+                                         int32_t num_splits) {
+  if (check_layer(kv, pt, params) != RBA_OK || max_seq_len < 0 || num_splits < 0) return 0;
+  return plan_splits(kv, pt, max_seq_len, params, num_splits).splits;
+}
+
+RBA_EXPORT size_t rba_decode_workspace_size(const rba_kv_cache *kv, const rba_page_table *pt,
+                                            int32_t max_seq_len, const rba_attn_params *params,
+                                            int32_t num_splits) {
+  if (check_layer(kv, pt, params) != RBA_OK || max_seq_len < 0 || num_splits < 0) return 0;
+  const SplitPlan sp = plan_splits(kv, pt, max_seq_len, params, num_splits);
+  return workspace_bytes_for(kv, pt, params, sp.splits);
+}
+
+RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
+                                 int32_t max_seq_len, const void *bias,
+                                 const rba_attn_params *params, int32_t num_splits,
+                                 void *workspace, size_t workspace_bytes, void *out, float *lse,
+                                 hipStream_t stream) {
+  rba_status st = check_layer(kv, pt, params);
+  if (st != RBA_OK) return st;
+  if (max_seq_len < 0 || num_splits < 0) return RBA_ERR_INVALID_ARG;
+  if (pt->num_seqs == 0) return RBA_OK;
+  if (q == nullptr || bias == nullptr || out == nullptr || pt->seq_lens == nullptr)
+    return RBA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(bias) || !aligned16(out) || !pool_ok(kv, pt))
+    return RBA_ERR_INVALID_ARG;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
+  if ((long long)max_seq_len > (long long)pt->max_pages_per_seq * pt->page_size)
+    return RBA_ERR_INVALID_ARG;
+
+  const SplitPlan sp = plan_splits(kv, pt, max_seq_len, params, num_splits);
+  const size_t need = workspace_bytes_for(kv, pt, params, sp.splits);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return RBA_ERR_WORKSPACE;
+  }
+
+  rba::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = kv->k_pool;
+  a.v_pool = kv->v_pool;
+  a.block_table = pt->block_table;
+  a.seq_lens = pt->seq_lens;
+  a.bias = bias;
+  a.out = out;
+  a.lse = lse;
+  a.num_seqs = pt->num_seqs;
+  a.Hq = params->num_q_heads;
+  a.Hkv = kv->num_kv_heads;
+  a.G = a.Hq / a.Hkv;
+  a.max_pages = pt->max_pages_per_seq;
+  a.page_size = pt->page_size;
+  a.log2_page = ilog2(pt->page_size);
+  a.window = params->window > 0 ? params->window : 0;
+  a.R = params->rel_extent;
+  a.sm_scale = params->sm_scale;
+  a.num_splits = sp.splits;
+  a.chunk_pages = sp.chunk_pages;
+  a.head_groups = (a.G + 3) / 4;
+  if (need > 0) {
+    const size_t rows = (size_t)a.num_seqs * a.Hq;
+    const size_t o_bytes = rows * sp.splits * kv->head_dim * sizeof(float);
+    a.part_o = static_cast<float *>(workspace);
+    a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                           ((o_bytes + 255) & ~(size_t)255));
+  }
+
+  hipError_t err;
+  if (kv->dtype == RBA_F32) {
+    err = rba::launch_decode_f32(a, kv->head_dim, stream);
+  } else {
+    const long long items = (long long)a.num_seqs * a.Hkv * a.num_splits * a.head_groups;
+    if (items > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
+    err = rba::launch_decode_bf16(a, kv->head_dim, stream);
+    if (err == hipSuccess && sp.splits > 1) err = rba::launch_merge(a, kv->head_dim, true, stream);
+  }
+  return err == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}

@@ -1,0 +1,53 @@
+// Internal declarations shared by the host entry points and the kernels of
+// librba.  Not part of the public ABI (include/rba.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rba {
+
+// Arguments of the prefill kernels.  Pointers are device pointers.
+struct PrefillArgs {
+  const void *q;             // [T][Hq][D]
+  const int32_t *cu_seqlens; // [B+1]
+  const void *k_pool;        // [num_pages][Hkv][P][D]
+  const void *v_pool;
+  const int32_t *block_table; // [B][max_pages]
+  const void *bias;          // [T][Hq][R]
+  void *out;                 // [T][Hq][D]
+  float *lse;                // [T][Hq] or null
+  int32_t num_seqs, Hq, Hkv, G, max_pages, page_size, log2_page;
+  int32_t window, R;
+  int32_t num_qtiles;        // query tiles per (sequence, head)
+  int32_t num_blocks;        // total work-groups of the launch
+  float sm_scale;
+};
+
+// Arguments of the decode kernels.
+struct DecodeArgs {
+  const void *q;             // [B][Hq][D]
+  const void *k_pool;
+  const void *v_pool;
+  const int32_t *block_table;
+  const int32_t *seq_lens;   // [B]
+  const void *bias;          // [B][Hq][R]
+  void *out;                 // [B][Hq][D]
+  float *lse;                // [B][Hq] or null
+  float *part_o;             // [B][Hq][S][D] when S > 1
+  float *part_lse;           // [B][Hq][S]   when S > 1
+  int32_t num_seqs, Hq, Hkv, G, max_pages, page_size, log2_page;
+  int32_t window, R;
+  int32_t num_splits;        // S
+  int32_t chunk_pages;       // pages per partition
+  int32_t head_groups;       // ceil(G / 4): query-head groups per KV head
+  float sm_scale;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs &a, int head_dim, hipStream_t s);
+
+}  // namespace rba

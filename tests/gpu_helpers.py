@@ -1,0 +1,111 @@
+"""Shared pieces of the GPU tests: running the HIP path, running the oracle
+on the same seeded inputs, and the parity bar.
+
+Tolerances (on the final output, against the fp64 oracle, unrounded):
+  bf16: max |gpu - ref| <= 2e-2 and sum|gpu - ref| / sum|ref| <= 5e-3
+  fp32: max |gpu - ref| <= 1e-5
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rba_inputs as ri
+import relative_position_bias_paged_amd as rba
+
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_REL = 5e-3
+F32_MAX_ABS = 1e-5
+LSE_MAX_ABS = 2e-2
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def errors(gpu: torch.Tensor, ref: np.ndarray):
+    g = gpu.detach().float().cpu().double().numpy()
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    diff = np.abs(g - ref)
+    return float(diff.max(initial=0.0)), float(diff.sum() / max(np.abs(ref).sum(), 1e-300))
+
+
+def assert_parity(gpu: torch.Tensor, ref: np.ndarray, dtype, what=""):
+    max_abs, mean_rel = errors(gpu, ref)
+    if dtype == torch.float32:
+        assert max_abs <= F32_MAX_ABS, f"{what}: max|d| {max_abs:.3e} > {F32_MAX_ABS}"
+    else:
+        assert max_abs <= BF16_MAX_ABS, f"{what}: max|d| {max_abs:.3e} > {BF16_MAX_ABS}"
+        assert mean_rel <= BF16_MEAN_REL, f"{what}: mean rel {mean_rel:.3e} > {BF16_MEAN_REL}"
+    return max_abs, mean_rel
+
+
+def gpu_prefill(case: ri.PrefillCase, want_lse=False, block_table=None, k_pool=None, v_pool=None):
+    sp = case.spec
+    lse = None
+    if want_lse:
+        lse = torch.empty((case.total_tokens, sp.num_q_heads), dtype=torch.float32,
+                          device=case.q.device)
+    out = rba.prefill(case.q, case.cu_seqlens, case.max_seqlen,
+                      case.k_pool if k_pool is None else k_pool,
+                      case.v_pool if v_pool is None else v_pool,
+                      case.block_table if block_table is None else block_table,
+                      case.seq_lens_dev, case.bias, window=sp.window, sm_scale=sp.scale(),
+                      lse=lse)
+    return (out, lse) if want_lse else out
+
+
+def oracle_prefill(case: ri.PrefillCase, rows=None, want_lse=False):
+    sp = case.spec
+    return oracle.prefill(case.q, case.k_log, case.v_log, case.bias, case.cu_list(),
+                          window=sp.window, rel_extent=sp.rel_extent, sm_scale=sp.scale(),
+                          rows=rows, want_lse=want_lse)
+
+
+def gpu_decode(case: ri.DecodeCase, num_splits=0, want_lse=False, block_table=None,
+               k_pool=None, v_pool=None, max_seq_len=None):
+    sp = case.spec
+    lse = None
+    if want_lse:
+        lse = torch.empty(case.q.shape[:2], dtype=torch.float32, device=case.q.device)
+    out = rba.decode(case.q, case.k_pool if k_pool is None else k_pool,
+                     case.v_pool if v_pool is None else v_pool,
+                     case.block_table if block_table is None else block_table,
+                     case.seq_lens_dev, case.max_seq_len if max_seq_len is None else max_seq_len,
+                     case.bias, window=sp.window, sm_scale=sp.scale(), num_splits=num_splits,
+                     lse=lse)
+    return (out, lse) if want_lse else out
+
+
+def oracle_decode(case: ri.DecodeCase, seqs=None, heads=None, want_lse=False):
+    """Oracle rows for the given sequences (all by default) and heads.
+
+    Returns an array [len(seqs), len(heads), D] (and lse [len(seqs), len(heads)]).
+    """
+    sp = case.spec
+    B = len(case.seq_lens)
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    heads = list(range(sp.num_q_heads)) if heads is None else list(heads)
+    ks, vs, cu = [], [], [0]
+    for b in seqs:
+        k, v = case.logical_kv(b)
+        ks.append(k)
+        vs.append(v)
+        cu.append(cu[-1] + case.seq_lens[b])
+    k = torch.cat(ks, 0)
+    v = torch.cat(vs, 0)
+    idx = torch.tensor(seqs, dtype=torch.long, device=case.q.device)
+    q = case.q.index_select(0, idx)
+    bias = case.bias.index_select(0, idx)
+    rows = [(i, h) for i in range(len(seqs)) for h in heads]
+    res = oracle.decode(q, k, v, bias, cu, window=sp.window, rel_extent=sp.rel_extent,
+                        sm_scale=sp.scale(), rows=rows, want_lse=want_lse)
+    if want_lse:
+        out, lse = res
+        return (out.reshape(len(seqs), len(heads), -1), lse.reshape(len(seqs), len(heads)))
+    return res.reshape(len(seqs), len(heads), -1)

@@ -1,0 +1,182 @@
+"""The C ABI on the host: the library loads, exports every symbol that
+include/rba.h declares, and rejects bad arguments before enqueuing anything.
+
+No call here reaches a kernel launch: every one fails host validation first
+(or only queries sizes), so these tests run without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import relative_position_bias_paged_amd as rba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rba.h")
+FAKE = 1 << 20          # a non-null, 16-byte aligned stand-in address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_functions() == sorted(rba.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rba.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", rba.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (rba_\w+)", out))
+    assert set(declared_functions()) <= exported
+    # nothing else of ours leaks out
+    assert exported == set(declared_functions())
+
+
+def _layer(hq=32, hkv=8, d=128, page=64, R=1024, W=0, scale=0.088, dtype=rba.RBA_BF16,
+           seqs=2, max_pages=256, pages=512, kp=FAKE, vp=FAKE, table=FAKE, lens=FAKE):
+    kv = rba.rba_kv_cache(kp, vp, hkv, d, dtype)
+    pt = rba.rba_page_table(table, lens, seqs, max_pages, page, pages)
+    prm = rba.rba_attn_params(hq, W, R, scale)
+    return kv, pt, prm
+
+
+def _prefill(kv, pt, prm, q=FAKE, cu=FAKE, T=100, max_len=50, bias=FAKE, out=FAKE, lse=None):
+    return rba.load().rba_prefill(q, cu, T, max_len, ctypes.byref(kv), ctypes.byref(pt), bias,
+                                  ctypes.byref(prm), out, lse, None)
+
+
+def _decode(kv, pt, prm, q=FAKE, max_len=1000, bias=FAKE, splits=0, ws=None, ws_bytes=0,
+            out=FAKE, lse=None):
+    return rba.load().rba_decode(q, ctypes.byref(kv), ctypes.byref(pt), max_len, bias,
+                                 ctypes.byref(prm), splits, ws, ws_bytes, out, lse, None)
+
+
+@pytest.mark.parametrize("change,expected", [
+    (dict(hq=30, hkv=8), rba.RBA_ERR_INVALID_ARG),        # Hq % Hkv != 0
+    (dict(hkv=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(page=48), rba.RBA_ERR_INVALID_ARG),             # not a power of two
+    (dict(page=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(R=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(scale=0.0), rba.RBA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), rba.RBA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), rba.RBA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), rba.RBA_ERR_INVALID_ARG),
+    (dict(dtype=7), rba.RBA_ERR_INVALID_ARG),
+    (dict(d=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(d=96), rba.RBA_ERR_UNSUPPORTED),
+    (dict(d=256), rba.RBA_ERR_UNSUPPORTED),
+    (dict(page=8), rba.RBA_ERR_UNSUPPORTED),
+    (dict(page=2048), rba.RBA_ERR_UNSUPPORTED),
+    (dict(kp=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(vp=FAKE + 2), rba.RBA_ERR_INVALID_ARG),         # misaligned pool
+    (dict(table=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(max_pages=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(pages=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(seqs=-1), rba.RBA_ERR_INVALID_ARG),
+])
+def test_layer_validation(change, expected):
+    kv, pt, prm = _layer(**change)
+    assert _prefill(kv, pt, prm) == expected
+    assert _decode(kv, pt, prm) == expected
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(q=0), dict(cu=0), dict(bias=0), dict(out=0), dict(q=FAKE + 8), dict(bias=FAKE + 2),
+    dict(out=FAKE + 4), dict(lse=FAKE + 2), dict(T=-1), dict(max_len=-3),
+    dict(max_len=256 * 64 + 1),                          # beyond the page table's reach
+])
+def test_prefill_argument_errors(kwargs):
+    kv, pt, prm = _layer()
+    assert _prefill(kv, pt, prm, **kwargs) == rba.RBA_ERR_INVALID_ARG
+
+
+def test_prefill_empty_is_noop():
+    kv, pt, prm = _layer()
+    assert _prefill(kv, pt, prm, q=0, cu=0, bias=0, out=0, T=0) == rba.RBA_OK
+    kv, pt, prm = _layer(seqs=0)
+    assert _prefill(kv, pt, prm, q=0, cu=0, bias=0, out=0) == rba.RBA_OK
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(q=0), dict(bias=0), dict(out=0), dict(q=FAKE + 2), dict(max_len=-1), dict(splits=-2),
+    dict(max_len=256 * 64 + 1),
+])
+def test_decode_argument_errors(kwargs):
+    kv, pt, prm = _layer()
+    assert _decode(kv, pt, prm, **kwargs) == rba.RBA_ERR_INVALID_ARG
+
+
+def test_decode_needs_seq_lens():
+    kv, pt, prm = _layer(lens=0)
+    assert _decode(kv, pt, prm) == rba.RBA_ERR_INVALID_ARG
+
+
+def test_decode_workspace_errors():
+    kv, pt, prm = _layer(seqs=32, max_pages=2048, pages=65536)
+    lib = rba.load()
+    need = lib.rba_decode_workspace_size(ctypes.byref(kv), ctypes.byref(pt), 131072,
+                                         ctypes.byref(prm), 16)
+    assert need > 0
+    assert _decode(kv, pt, prm, max_len=131072, splits=16) == rba.RBA_ERR_WORKSPACE
+    assert _decode(kv, pt, prm, max_len=131072, splits=16, ws=FAKE, ws_bytes=need - 1) == \
+        rba.RBA_ERR_WORKSPACE
+    assert _decode(kv, pt, prm, max_len=131072, splits=16, ws=FAKE + 16, ws_bytes=need) == \
+        rba.RBA_ERR_WORKSPACE
+
+
+def test_decode_split_plan():
+    lib = rba.load()
+
+    def plan(max_len, splits, **kw):
+        kv, pt, prm = _layer(**kw)
+        n = lib.rba_decode_num_splits(ctypes.byref(kv), ctypes.byref(pt), max_len,
+                                      ctypes.byref(prm), splits)
+        ws = lib.rba_decode_workspace_size(ctypes.byref(kv), ctypes.byref(pt), max_len,
+                                           ctypes.byref(prm), splits)
+        return n, ws
+
+    # long-context global decode: 16 requested partitions of 128 pages each
+    n, ws = plan(131072, 16, seqs=32, max_pages=2048, pages=65536)
+    assert n == 16
+    rows = 32 * 32
+    assert ws == rows * 16 * 128 * 4 + rows * 16 * 4
+    # one partition: no workspace
+    assert plan(4096, 1, seqs=4)[1] == 0
+    # never more partitions than pages
+    assert plan(100, 64, seqs=4)[0] == 2
+    # local layer: the visible window spans at most 9 pages of 64
+    n, _ = plan(32768, 0, seqs=256, hkv=16, W=512, R=512, max_pages=512, pages=70000)
+    assert n == 1
+    # automatic split of a global layer at batch 256 and 32K context
+    n, _ = plan(32768, 0, seqs=256, max_pages=512, pages=70000)
+    assert 1 < n <= 256
+    # fp32 runs unpartitioned
+    assert plan(131072, 16, seqs=32, max_pages=2048, pages=65536, dtype=rba.RBA_F32) == (1, 0)
+    # invalid arguments report 0
+    assert plan(1000, 0, hq=31) == (0, 0)
+
+
+def test_status_strings():
+    for code, name in [(0, "RBA_OK"), (1, "RBA_ERR_INVALID_ARG"), (2, "RBA_ERR_UNSUPPORTED"),
+                       (3, "RBA_ERR_WORKSPACE"), (4, "RBA_ERR_HIP")]:
+        assert rba.status_string(code) == name
+    assert rba.status_string(99) == "RBA_UNKNOWN_STATUS"
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((4, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        rba.prefill(q, torch.zeros(2, dtype=torch.int32), 4,
+                    torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16),
+                    torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16),
+                    torch.zeros((1, 1), dtype=torch.int32), None,
+                    torch.zeros((4, 2, 8), dtype=torch.bfloat16), window=0, sm_scale=0.1)

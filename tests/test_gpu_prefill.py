@@ -1,0 +1,185 @@
+"""GPU parity of rba_prefill against the CPU oracle (same seeded inputs).
+
+Sizes span several 128-query and 64-key tiles with ragged tails, windows and
+bias extents that are not tile multiples, page sizes below, at and above the
+64-key tile, the clamped-bucket region of global layers, GQA 1..4, and the
+degenerate cases (one-token sequences, an empty sequence, rel_extent 1,
+window 1).
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import rba_inputs as ri
+from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, errors, gpu_prefill,
+                         oracle_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(hq, hkv, d, W, R, P, dtype=torch.bfloat16, **kw):
+    return ri.LayerSpec(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, window=W, rel_extent=R,
+                        page_size=P, dtype=dtype, **kw)
+
+
+CASES = [
+    # id, spec, lens, pool pages (None = exact)
+    ("local-w100-r100-p64", spec(8, 4, 128, 100, 100, 64), [1, 130, 700], None),
+    ("local-w256-p16", spec(4, 2, 128, 256, 256, 16), [300, 1000], 200),
+    ("local-w512-gqa2", spec(4, 2, 128, 512, 512, 64), [1500, 640], 64),
+    ("global-r128-clamp", spec(8, 2, 128, 0, 128, 64), [517, 1100], 40),
+    ("global-r1024-gqa4", spec(8, 2, 128, 0, 1024, 64), [2100], 40),
+    ("global-p128", spec(4, 1, 128, 0, 200, 128), [77, 900], 12),
+    ("global-p256-r64", spec(4, 4, 128, 0, 64, 256), [1024, 3], 8),
+    ("global-p32-mha", spec(2, 2, 128, 0, 256, 32), [333], 20),
+    ("d64-local", spec(4, 2, 64, 192, 192, 64), [400, 129], 16),
+    ("d64-global", spec(4, 1, 64, 0, 96, 16), [260], 20),
+    ("r1-degenerate", spec(4, 2, 128, 0, 1, 64), [200], 4),
+    ("r-odd-clamp", spec(4, 2, 128, 0, 37, 64), [300], 5),
+    ("window1", spec(4, 2, 128, 1, 8, 64), [150], 3),
+    ("empty-and-single", spec(4, 2, 128, 0, 64, 64), [0, 1, 65, 0, 2], 8),
+]
+
+
+@pytest.mark.parametrize("cid,sp,lens,pages", CASES, ids=[c[0] for c in CASES])
+def test_prefill_parity(cid, sp, lens, pages):
+    dev = device()
+    case = ri.make_prefill(sp, lens, seed=zlib.crc32(cid.encode()) % 100000, device=dev, num_pages=pages)
+    out, lse = gpu_prefill(case, want_lse=True)
+    torch.cuda.synchronize()
+    if case.total_tokens == 0:
+        return
+    ref, ref_lse = oracle_prefill(case, want_lse=True)
+    assert_parity(out, ref, sp.dtype, cid)
+    g_lse = lse.cpu().double().numpy()
+    assert np.max(np.abs(g_lse - ref_lse)) <= LSE_MAX_ABS, cid
+
+
+def test_prefill_fp32_tiny_workload():
+    """The tiny fp32 local layer: 256 tokens, 4/2 heads, head_dim 64, window 64."""
+    dev = device()
+    case = ri.build_workload("tiny-local-prefill-fp32", dev)["prefill"]
+    out, lse = gpu_prefill(case, want_lse=True)
+    ref, ref_lse = oracle_prefill(case, want_lse=True)
+    assert_parity(out, ref, torch.float32, "tiny fp32")
+    assert np.max(np.abs(lse.cpu().double().numpy() - ref_lse)) <= 1e-5
+
+
+@pytest.mark.parametrize("W", [0, 50])
+def test_prefill_fp32_ragged(W):
+    dev = device()
+    sp = spec(4, 2, 128, W, 40, 16, dtype=torch.float32)
+    case = ri.make_prefill(sp, [70, 1, 33], seed=77, device=dev, num_pages=12)
+    out = gpu_prefill(case)
+    assert_parity(out, oracle_prefill(case), torch.float32, f"fp32 W={W}")
+
+
+def test_page_table_bit_exact():
+    """Identity and shuffled page tables over the same logical K/V give the
+    bitwise-identical output: the arithmetic depends only on key positions."""
+    dev = device()
+    sp = spec(8, 2, 128, 0, 256, 64)
+    lens = [700, 300]
+    a = ri.make_prefill(sp, lens, seed=5, device=dev, num_pages=20, shuffle=False)
+    b = ri.make_prefill(sp, lens, seed=5, device=dev, num_pages=20, shuffle=True)
+    assert not torch.equal(a.block_table, b.block_table)
+    assert torch.equal(a.q, b.q) and torch.equal(a.bias, b.bias)
+    oa = gpu_prefill(a)
+    ob = gpu_prefill(b)
+    torch.cuda.synchronize()
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_masked_positions_cannot_leak():
+    """NaN in every pool slot no key reaches, and in bias buckets no row uses,
+    leaves the output bit-identical (masks select, never multiply)."""
+    dev = device()
+    sp = spec(4, 2, 128, 96, 96, 64)
+    case = ri.make_prefill(sp, [150, 77], seed=11, device=dev, num_pages=10)
+    # the generator already NaN-fills unowned pages and tail slots; build a
+    # twin whose unreachable slots hold zeros instead
+    k0 = torch.nan_to_num(case.k_pool, nan=0.0)
+    v0 = torch.nan_to_num(case.v_pool, nan=0.0)
+    assert torch.isnan(case.k_pool).any()
+    o_nan = gpu_prefill(case)
+    o_zero = gpu_prefill(case, k_pool=k0, v_pool=v0)
+    # bias buckets a row never reads: d > t (none for W = R here except the
+    # first rows), set them to NaN
+    bias2 = case.bias.clone()
+    for tok, t in ((0, 0), (1, 1), (150, 0), (151, 1)):
+        bias2[tok, :, t + 1:] = float("nan")
+    case2 = ri.PrefillCase(**{**case.__dict__, "bias": bias2})
+    o_bias = gpu_prefill(case2)
+    torch.cuda.synchronize()
+    assert torch.equal(o_nan.view(torch.int16), o_zero.view(torch.int16))
+    assert torch.equal(o_nan.view(torch.int16), o_bias.view(torch.int16))
+
+
+def test_window_one_returns_value_exactly():
+    """window 1: each query sees only itself, so out[t,h] = v[t, h // G] bitwise."""
+    dev = device()
+    sp = spec(8, 2, 128, 1, 16, 64)
+    case = ri.make_prefill(sp, [200, 3], seed=13, device=dev, num_pages=6)
+    out = gpu_prefill(case)
+    ref = case.v_log.repeat_interleave(4, dim=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_row_constant_bias_shift():
+    """Adding a constant to a whole bias row changes nothing beyond rounding."""
+    dev = device()
+    sp = spec(4, 2, 128, 0, 128, 64)
+    case = ri.make_prefill(sp, [300], seed=17, device=dev, num_pages=5)
+    c = torch.randint(-4, 5, (300, 4, 1), device=dev).to(torch.bfloat16)
+    bias2 = (case.bias.float() + c.float()).to(torch.bfloat16)
+    case2 = ri.PrefillCase(**{**case.__dict__, "bias": bias2})
+    o1 = gpu_prefill(case)
+    o2 = gpu_prefill(case2)
+    ref2 = oracle_prefill(case2)
+    assert_parity(o2, ref2, torch.bfloat16, "shifted")
+    max_abs, _ = errors(o1, o2.double().cpu().numpy())
+    # the shifted bias is itself rounded to bf16, so rows may move by rounding
+    assert max_abs <= 2e-2
+
+
+def test_zero_bias_is_plain_attention():
+    """Zero bias: the kernel reproduces plain causal attention (torch SDPA in fp32)."""
+    dev = device()
+    sp = spec(4, 2, 128, 0, 64, 64)
+    case = ri.make_prefill(sp, [257], seed=19, device=dev, num_pages=5)
+    case.bias.zero_()
+    out = gpu_prefill(case)
+    q = case.q.float().permute(1, 0, 2).contiguous()
+    k = case.k_log.float().repeat_interleave(2, 1).permute(1, 0, 2).contiguous()
+    v = case.v_log.float().repeat_interleave(2, 1).permute(1, 0, 2).contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q.cpu(), k.cpu(), v.cpu(), is_causal=True, scale=1 / math.sqrt(128))
+    assert_parity(out, ref.permute(1, 0, 2).double().numpy(), torch.bfloat16, "zero bias")
+
+
+@pytest.mark.parametrize("name", ["local-prefill-4x4096", "global-prefill-2x16384"])
+def test_full_size_workload_sampled(name):
+    """The full-size prefill workloads, in the launch configuration the
+    benchmark times, checked on sampled rows (every sequence, every head,
+    first/last tokens, tile edges and random positions)."""
+    dev = device()
+    case = ri.build_workload(name, dev)["prefill"]
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    g = torch.Generator().manual_seed(3)
+    cu = case.cu_list()
+    rows = []
+    for b in range(len(case.seq_lens)):
+        L = case.seq_lens[b]
+        ts = {0, 1, 63, 64, 127, 128, 511, 512, 1023, 1024, L - 2, L - 1}
+        ts |= set(torch.randint(0, L, (6,), generator=g).tolist())
+        for t in sorted(x for x in ts if 0 <= x < L):
+            h = int(torch.randint(0, case.spec.num_q_heads, (1,), generator=g))
+            rows.append((cu[b] + t, h))
+    ref = oracle_prefill(case, rows=rows)
+    sel = torch.stack([out[tok, h] for tok, h in rows])
+    assert_parity(sel, ref, torch.bfloat16, name)
