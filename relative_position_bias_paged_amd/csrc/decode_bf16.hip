@@ -68,7 +68,7 @@ __device__ __forceinline__ float lane_read(float x, int src_lane) {
 
 template <int D>
 struct TileBuf {
-  u32x4_t k[D / 32];                     // K[key = c16][(D/4)*g4 + 8*kk ..+8]
+  u32x4_t k[D / 32];                     // K[key = c16][32*kk + 8*g4 ..+8]
   uint32_t v[4][D / 32];                 // V[4*kg+i][(D/16)*dg ..+D/16], D/32 dwords each
   uint32_t bias[4];                      // raw bf16 bias of (head r, key c16)
 };
@@ -120,29 +120,37 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   const size_t page_stride = (size_t)a.Hkv * head_stride;
 
   // Q as the A operand: row i = c16 carries head (i & 3) of this group.
+  // k-slot group g4 of MFMA kk holds head-dim elements 32*kk + 8*g4 .. +8.
   const int qr = c16 & 3;
   u32x4_t qa[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    qa[kk] = (qr < nh) ? *reinterpret_cast<const u32x4_t *>(
-                             qp + ((size_t)b * Hq + h_base + qr) * D + (D / 4) * g4 + 8 * kk)
-                       : u32x4_t{0, 0, 0, 0};
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+        qp + ((size_t)b * Hq + h_base + min(qr, nh - 1)) * D + 32 * kk + 8 * g4);
+    qa[kk] = (qr < nh) ? v : u32x4_t{0, 0, 0, 0};
   }
+  // bias rows of the (up to 4) heads; heads past nh reuse the last one
+  const uint16_t *brow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) brow[r] = bp + ((size_t)b * Hq + h_base + min(r, nh - 1)) * R;
   float b_last[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    b_last[r] = (r < nh && n > 0) ? bf16_to_f32(bp[((size_t)b * Hq + h_base + r) * R + (R - 1)]) : 0.f;
+  for (int r = 0; r < 4; ++r) b_last[r] = bf16_to_f32(brow[r][R - 1]);
 
   TileBuf<D> buf[NBUF];
 
+  // Every load is unconditional: a tile index past the end re-reads the last
+  // tile (already in cache), heads past nh read a valid row, and clamp-only
+  // tiles read bucket R-1, so no load sits behind a branch and the waits
+  // before each tile's use only cover that tile.
   auto issue = [&](int ti, TileBuf<D> &tb) {
-    const int ts = k_lo + ti * 16;                      // first key of the tile
+    const int ts = k_lo + min(ti, ntiles - 1) * 16;     // first key of the tile
     const int page = trow[ts >> lp];
     const size_t base = (size_t)page * page_stride + (size_t)kvh * head_stride +
                         (size_t)(ts & (P - 1)) * D;
-    const uint16_t *kt = kp + base + (size_t)c16 * D + (D / 4) * g4;
+    const uint16_t *kt = kp + base + (size_t)c16 * D + 8 * g4;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) tb.k[kk] = *reinterpret_cast<const u32x4_t *>(kt + 8 * kk);
+    for (int kk = 0; kk < KK; ++kk) tb.k[kk] = *reinterpret_cast<const u32x4_t *>(kt + 32 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint16_t *vt = vp + base + (size_t)(4 * g4 + i) * D + DV * c16;
@@ -157,12 +165,9 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
     // bias of this lane's key for each head; tiles entirely at distance
     // >= R-1 use b_last and skip the load
     const bool band = (t - (ts + 15)) < R - 1;
+    const int idx = band ? min(max(t - (ts + c16), 0), R - 1) : R - 1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = t - (ts + c16);
-      const int idx = min(max(d, 0), R - 1);
-      tb.bias[r] = (band && r < nh) ? (uint32_t)bp[((size_t)b * Hq + h_base + r) * R + idx] : 0u;
-    }
+    for (int r = 0; r < 4; ++r) tb.bias[r] = brow[r][idx];
   };
 
   float acc[4][DV];
@@ -234,16 +239,15 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   };
 
   // software pipeline: NBUF tiles in flight
+  if (ntiles > 0) {
 #pragma unroll
-  for (int j = 0; j < NBUF; ++j)
-    if (j < ntiles) issue(j, buf[j]);
-  for (int i0 = 0; i0 < ntiles; i0 += NBUF) {
+    for (int j = 0; j < NBUF; ++j) issue(j, buf[j]);
+    for (int i0 = 0; i0 < ntiles; i0 += NBUF) {
 #pragma unroll
-    for (int j = 0; j < NBUF; ++j) {
-      const int ti = i0 + j;
-      if (ti < ntiles) {
-        process(ti, buf[j]);
-        if (ti + NBUF < ntiles) issue(ti + NBUF, buf[j]);
+      for (int j = 0; j < NBUF; ++j) {
+        const int ti = i0 + j;
+        if (ti < ntiles) process(ti, buf[j]);
+        issue(ti + NBUF, buf[j]);
       }
     }
   }

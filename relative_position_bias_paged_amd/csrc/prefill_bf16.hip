@@ -27,6 +27,8 @@
 //    than 2^8), which is exact because numerator and denominator share it.
 #include "rba_internal.h"
 
+#include <type_traits>
+
 namespace rba {
 namespace {
 
@@ -49,11 +51,13 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <int D>
@@ -63,7 +67,7 @@ struct __align__(16) PrefillSmem {
   uint16_t ring[BM * RING];     // bias ring
 };
 
-template <int D>
+template <int D, bool BIG_PAGE, bool VEC_BIAS>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
   constexpr int KPT = BN * CHUNKS / NTHREADS;   // key rows per thread per tile
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
 
   // Work-group -> (sequence, head, query tile).  Blocks are dealt to the 8
   // XCDs round-robin; remap so each XCD walks a contiguous range, in which
@@ -110,12 +114,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const uint16_t *qp = static_cast<const uint16_t *>(a.q);
   const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
   const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
-  const uint16_t *bp = static_cast<const uint16_t *>(a.bias);
   const int32_t *trow = a.block_table + (size_t)b * a.max_pages;
   const int P = a.page_size;
   const int lp = a.log2_page;
   const size_t head_stride = (size_t)P * D;           // elements per (page, head)
   const size_t page_stride = (size_t)a.Hkv * head_stride;
+  // bias rows of this work-group start here; row q adds q * Hq * R
+  const uint16_t *bwg = static_cast<const uint16_t *>(a.bias) +
+                        ((size_t)(tok0 + t0) * Hq + h) * R;
+  const uint32_t brow_stride = (uint32_t)Hq * (uint32_t)R;
 
   // ---- this lane's query row --------------------------------------------
   const int col = lane & 31;
@@ -128,57 +135,57 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   u32x4_t qf[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    qf[kb] = row_ok ? *reinterpret_cast<const u32x4_t *>(qp + row * D + kb * 16 + half * 8)
-                    : u32x4_t{0, 0, 0, 0};
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qp + row * D + kb * 16 + half * 8);
+    qf[kb] = row_ok ? v : u32x4_t{0, 0, 0, 0};
   }
-  const float b_last = row_ok ? bf16_to_f32(bp[row * R + (R - 1)]) : 0.f;
+  const float b_last = bf16_to_f32(bwg[(row_ok ? (uint32_t)q_local : 0u) * brow_stride + (R - 1)]);
 
-  // ---- K/V tile loaders ----------------------------------------------------
+  // ---- K/V tile loaders (every load unconditional; rows past the end of
+  // the sequence are read from inside the same page, then zeroed) ----------
   const int kc = tid % CHUNKS;          // 16-byte chunk this thread moves
   const int krow0 = tid / CHUNKS;       // K rows krow0 + j*(NTHREADS/CHUNKS)
   const int vkey0 = (tid / CHUNKS) * KPT;  // V keys vkey0 .. vkey0+KPT-1
 
   u32x4_t kreg[KPT], vreg[KPT];
-
-  auto kv_offset = [&](int s) -> size_t {  // element offset of key s, chunk kc
-    const int page = trow[s >> lp];
-    return (size_t)page * page_stride + (size_t)kvh * head_stride +
-           (size_t)(s & (P - 1)) * D + kc * 8;
-  };
+  const u32x4_t zero4 = {0, 0, 0, 0};
 
   auto load_kv = [&](int s0) {
-    if (P >= BN) {
+    if constexpr (BIG_PAGE) {
       const int page = trow[s0 >> lp];
-      const size_t pb = (size_t)page * page_stride + (size_t)kvh * head_stride +
-                        (size_t)(s0 & (P - 1)) * D + kc * 8;
+      const uint16_t *kt = kp + (size_t)page * page_stride + (size_t)kvh * head_stride +
+                           (size_t)(s0 & (P - 1)) * D;
+      const uint16_t *vt = vp + (kt - kp);
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int kr = krow0 + j * (NTHREADS / CHUNKS);
-        kreg[j] = (s0 + kr < L) ? *reinterpret_cast<const u32x4_t *>(kp + pb + (size_t)kr * D)
-                                : u32x4_t{0, 0, 0, 0};
-        const int vk = vkey0 + j;
-        vreg[j] = (s0 + vk < L) ? *reinterpret_cast<const u32x4_t *>(vp + pb + (size_t)vk * D)
-                                : u32x4_t{0, 0, 0, 0};
+        kreg[j] = *reinterpret_cast<const u32x4_t *>(kt + (uint32_t)(kr * D + kc * 8));
+        vreg[j] = *reinterpret_cast<const u32x4_t *>(vt + (uint32_t)((vkey0 + j) * D + kc * 8));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
         const int kr = krow0 + j * (NTHREADS / CHUNKS);
-        kreg[j] = (s0 + kr < L) ? *reinterpret_cast<const u32x4_t *>(kp + kv_offset(s0 + kr))
-                                : u32x4_t{0, 0, 0, 0};
-        const int vk = vkey0 + j;
-        vreg[j] = (s0 + vk < L) ? *reinterpret_cast<const u32x4_t *>(vp + kv_offset(s0 + vk))
-                                : u32x4_t{0, 0, 0, 0};
+        const int sk = min(s0 + kr, L - 1);
+        const size_t ko = (size_t)trow[sk >> lp] * page_stride + (size_t)kvh * head_stride +
+                          (size_t)(sk & (P - 1)) * D + kc * 8;
+        kreg[j] = *reinterpret_cast<const u32x4_t *>(kp + ko);
+        const int sv = min(s0 + vkey0 + j, L - 1);
+        const size_t vo = (size_t)trow[sv >> lp] * page_stride + (size_t)kvh * head_stride +
+                          (size_t)(sv & (P - 1)) * D + kc * 8;
+        vreg[j] = *reinterpret_cast<const u32x4_t *>(vp + vo);
       }
     }
   };
 
-  auto commit_kv = [&]() {
+  // Rows at or past the end of the sequence are zeroed here, at the LDS
+  // write, so the loads themselves stay unconditional and in flight.
+  auto commit_kv = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int kr = krow0 + j * (NTHREADS / CHUNKS);
       const int phys = kc ^ (kr & (CHUNKS - 1));
-      *reinterpret_cast<u32x4_t *>(&sm.k[kr * D + phys * 8]) = kreg[j];
+      *reinterpret_cast<u32x4_t *>(&sm.k[kr * D + phys * 8]) = (s0 + kr < L) ? kreg[j] : zero4;
+      vreg[j] = (s0 + vkey0 + j < L) ? vreg[j] : zero4;
     }
     // V^T: element (key, d) -> vt[d][key]; this thread holds keys
     // vkey0..vkey0+KPT-1 of head-dim chunk kc.
@@ -202,43 +209,45 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // For key tile s0, row q needs distances t0+q-s0-63 .. t0+q-s0, i.e. the
   // chunks lo(q) = floor((t0-s0-63+q)/64) and lo(q)+1.  Moving to the next
   // tile (s0 += 64) needs chunk lo-1 and drops lo+1: same ring slot.
+  // Thread tid moves 16-byte piece (tid & 7) of rows tid/8 + 32*j.
   u32x4_t breg[4];
-  const bool r_vec = (R & 7) == 0;
+  const int bq0 = tid >> 3;
+  const int bv8 = (tid & 7) * 8;
 
-  auto chunk_of = [&](int s0, int q, int which) { return ((t0 - s0 - (BN - 1) + q) >> 6) + which; };
+  auto chunk_elem = [&](int s0, int q, int which) {
+    return (((t0 - s0 - (BN - 1) + q) >> 6) + which) * BN + bv8;
+  };
 
   auto load_chunk = [&](int s0, int which) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int u = tid + j * NTHREADS;
-      const int q = u >> 3, v = u & 7;
-      const int e = chunk_of(s0, q, which) * BN + v * 8;
+      const int q = bq0 + 32 * j;
+      const int e = chunk_elem(s0, q, which);
       const bool ok = (t0 + q < L) && e >= 0 && e < R;
-      u32x4_t val = {0, 0, 0, 0};
-      if (ok) {
-        const uint16_t *src = bp + ((size_t)tok0 + t0 + q) * Hq * R + (size_t)h * R + e;
-        if (r_vec) {
-          val = *reinterpret_cast<const u32x4_t *>(src);
-        } else {
+      if constexpr (VEC_BIAS) {
+        const uint32_t off = ok ? (uint32_t)q * brow_stride + (uint32_t)e : 0u;
+        breg[j] = *reinterpret_cast<const u32x4_t *>(bwg + off);
+      } else {
+        u32x4_t v = zero4;
 #pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const uint32_t el = (e + x < R) ? (uint32_t)src[x] : 0u;
-            val[x >> 1] |= el << ((x & 1) * 16);
-          }
+        for (int x = 0; x < 8; ++x) {
+          const bool okx = ok && (e + x < R);
+          const uint32_t off = okx ? (uint32_t)q * brow_stride + (uint32_t)(e + x) : 0u;
+          const uint32_t el = bwg[off];
+          v[x >> 1] |= (okx ? el : 0u) << ((x & 1) * 16);
         }
+        breg[j] = v;
       }
-      breg[j] = val;
     }
   };
 
   auto commit_chunk = [&](int s0, int which) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int u = tid + j * NTHREADS;
-      const int q = u >> 3, v = u & 7;
-      const int e = chunk_of(s0, q, which) * BN + v * 8;
-      if ((t0 + q < L) && e >= 0 && e < R)
-        *reinterpret_cast<u32x4_t *>(&sm.ring[q * RING + (e & (RING - 1))]) = breg[j];
+      const int q = bq0 + 32 * j;
+      const int e = chunk_elem(s0, q, which);
+      const bool ok = (t0 + q < L) && e >= 0 && e < R;
+      *reinterpret_cast<u32x4_t *>(&sm.ring[q * RING + (e & (RING - 1))]) = ok ? breg[j] : zero4;
     }
   };
 
@@ -261,43 +270,67 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     const bool need_mask = (dmin_w < 0) || (W > 0 && dmax_w >= W) || (s0 + BN > L);
     const bool band = dmin_w < R - 1;
 
-    // S^T = K Q^T : two 32x32 blocks of keys x queries
+    // S^T = K Q^T : two 32x32 blocks of keys x queries; K fragments are read
+    // from LDS one k-step ahead of the MFMAs that consume them
     f32x16_t sacc[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int j = 0; j < 16; ++j) sacc[sub][j] = 0.f;
-      const int key_row = sub * 32 + col;
+    const int kbase0 = col * D;                // key row s0 + col; sub 1 adds 32 rows
+    const int ksw = col & (CHUNKS - 1);        // (32 + col) & (CHUNKS-1) is the same
+    // 2*KB fragments (k-step kb, sub-block sub) streamed one ahead of the MFMAs
+    auto kfrag = [&](int step) {
+      const int kb = step >> 1, sub = step & 1;
+      return *reinterpret_cast<const u32x4_t *>(
+          &sm.k[kbase0 + sub * 32 * D + (((2 * kb + half) ^ ksw) * 8)]);
+    };
+    u32x4_t kf[2];
+    kf[0] = kfrag(0);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int phys = (2 * kb + half) ^ (key_row & (CHUNKS - 1));
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(&sm.k[key_row * D + phys * 8]);
-        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, kf), __builtin_bit_cast(bf16x8_t, qf[kb]), sacc[sub], 0, 0, 0);
-      }
+    for (int step = 0; step < 2 * KB; ++step) {
+      if (step + 1 < 2 * KB) kf[(step + 1) & 1] = kfrag(step + 1);
+      const int kb = step >> 1, sub = step & 1;
+      sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[step & 1]),
+                                                          __builtin_bit_cast(bf16x8_t, qf[kb]), sacc[sub], 0, 0, 0);
     }
 
-    // scores: scale, bias, mask
+    // scores: scale, bias, mask.  A key at offset koff = key - s0 - 4*half
+    // from this lane's first key is visible iff kv_lo < koff <= kv_hi; the
+    // band/clamp choice is hoisted out of the element loop.
     float mx = -INFINITY;
+    const int dq = t - s0 - 4 * half;          // distance of key s0 + 4*half
+    int kv_hi = min(dq, L - 1 - s0 - 4 * half);
+    int kv_lo = (W > 0) ? dq - W : -1000000;
+    if (!need_mask) { kv_hi = 1000000; kv_lo = -1000000; }
+    const uint16_t *ringrow = &sm.ring[q_local * RING];
+    auto scores = [&](auto band_c) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = s0 + sub * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
-        const int d = t - key;
-        float bv = b_last;
-        if (band) {
-          const float ringv = bf16_to_f32(sm.ring[q_local * RING + (d & (RING - 1))]);
-          bv = (d < R - 1) ? ringv : b_last;
+        for (int j = 0; j < 16; ++j) {
+          const int koff = sub * 32 + 8 * (j >> 2) + (j & 3);   // key - s0 - 4*half
+          float bv = b_last;
+          if constexpr (decltype(band_c)::value) {
+            const int d = dq - koff;
+            const float ringv = bf16_to_f32(ringrow[d & (RING - 1)]);
+            bv = (d < R - 1) ? ringv : b_last;
+          }
+          float x = fmaf(sacc[sub][j], scale, bv);
+          x = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
+          sacc[sub][j] = x;
         }
-        float x = fmaf(sacc[sub][j], scale, bv);
-        if (need_mask) {
-          const bool vis = (d >= 0) && (W <= 0 || d < W) && (key < L);
-          x = vis ? x : -INFINITY;
-        }
-        sacc[sub][j] = x;
-        mx = fmaxf(mx, x);
       }
+    };
+    if (band) scores(std::true_type{}); else scores(std::false_type{});
+    {
+      float m8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        m8[i] = fmaxf(fmaxf(sacc[i >> 2][(i & 3) * 4 + 0], sacc[i >> 2][(i & 3) * 4 + 1]),
+                      fmaxf(sacc[i >> 2][(i & 3) * 4 + 2], sacc[i >> 2][(i & 3) * 4 + 3]));
+      mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                 fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
 
@@ -314,32 +347,40 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
       m2 = mnew;
     }
+    {
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+      for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sub][j], LOG2E, -m2));
-        lsum += p;
-        sacc[sub][j] = p;
-      }
+        for (int j = 0; j < 16; ++j) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sub][j], LOG2E, -m2));
+          ps[j & 3] += p;
+          sacc[sub][j] = p;
+        }
+      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
 
     // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` are keys
     // ks*16 + 4*half + {0,1,2,3,8,9,10,11}: exactly S^T registers 8*(ks&1)+0..7.
+    const uint16_t *vtrow = &sm.vt[col * VT_STRIDE + 4 * half];
 #pragma unroll
     for (int ks = 0; ks < BN / 16; ++ks) {
       const int sub = ks >> 1, rb = (ks & 1) * 8;
+      u32x4_t vw[DSUB];
+#pragma unroll
+      for (int ds = 0; ds < DSUB; ++ds) {
+        const uint16_t *vr = vtrow + ds * 32 * VT_STRIDE + ks * 16;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 8);
+        vw[ds] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
       u32x4_t pw;
 #pragma unroll
       for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(sacc[sub][rb + 2 * j], sacc[sub][rb + 2 * j + 1]);
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
-      for (int ds = 0; ds < DSUB; ++ds) {
-        const int drow = ds * 32 + col;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(&sm.vt[drow * VT_STRIDE + ks * 16 + 4 * half]);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(&sm.vt[drow * VT_STRIDE + ks * 16 + 8 + 4 * half]);
-        const u32x4_t vw = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw), pb, oacc[ds], 0, 0, 0);
-      }
+      for (int ds = 0; ds < DSUB; ++ds)
+        oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw[ds]), pb, oacc[ds], 0, 0, 0);
     }
   };
 
@@ -350,7 +391,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   bool ring_ready = false;
   const bool band0 = wg_band(s_begin);
   if (band0) load_chunk(s_begin, 0);
-  commit_kv();
+  commit_kv(s_begin);
   if (band0) {
     commit_chunk(s_begin, 0);
     load_chunk(s_begin, 1);
@@ -370,7 +411,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     compute_tile(s0);
     __syncthreads();
     if (has_next) {
-      commit_kv();
+      commit_kv(sn);
       if (band_next) {
         commit_chunk(sn, 0);
         if (!ring_ready) {
@@ -404,12 +445,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
+template <int D>
+static void launch_d(const PrefillArgs &a, hipStream_t s) {
   dim3 grid(a.num_blocks), block(NTHREADS);
+  const bool big = a.page_size >= BN;
+  const bool vec = (a.R & 7) == 0;
+  if (big && vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, s, a);
+  else if (big) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, s, a);
+  else if (vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, s, a);
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
   if (head_dim == 128) {
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, s, a);
+    launch_d<128>(a, s);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, s, a);
+    launch_d<64>(a, s);
   } else {
     return hipErrorInvalidValue;
   }
