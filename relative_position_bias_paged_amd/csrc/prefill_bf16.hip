@@ -11,16 +11,22 @@
 // on _build_rel_logits.
 //
 // Work decomposition (one work-group = 4 waves = 128 queries of one head):
-//  * a 64-key K tile and the transposed V tile are staged through LDS,
-//    prefetched into registers one tile ahead;
+//  * 64-key K and V tiles are staged HBM -> registers (one tile ahead) ->
+//    LDS, both row-major with XOR-swizzled 16-byte chunks;
 //  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16, so each
 //    lane owns one query column: the softmax row statistics stay in a lane
 //    pair (lane, lane^32);
+//  * the V^T operand comes straight from the row-major V tile through the
+//    transposing LDS read ds_read_b64_tr_b16;
 //  * the bias of query row t at distance d sits in a per-row ring of two
-//    64-wide distance chunks in LDS (element d at d mod 128); each key tile
-//    brings in one new chunk per row, loaded with aligned 16-byte reads, so
-//    every bias element crosses HBM once.  Tiles whose distances all lie at
-//    or beyond R-1 use the single clamped value bias[t,h,R-1] instead;
+//    64-wide distance chunks in LDS, with the odd chunk mirrored in front of
+//    the even one so any four consecutive distances are contiguous; each key
+//    tile brings in one new chunk per row, loaded with aligned 16-byte reads,
+//    so every bias element crosses HBM once.  Tiles whose distances all lie
+//    at or beyond R-1 use the single clamped value bias[t,h,R-1];
+//  * three score paths chosen per wave and tile: clamp-only unmasked (scale,
+//    bias and max folded into one FMA before exp2), band unmasked, and a
+//    general path for window/causal/sequence-end edges and the clamp border;
 //  * masking selects (never multiplies), so NaN in keys past the end of a
 //    sequence or in masked positions cannot leak into the output;
 //  * the running max is rescaled lazily (only when a row's max grows by more
@@ -36,12 +42,13 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int BM = 128;        // queries per work-group
 constexpr int BN = 64;         // keys per tile (= one bias chunk)
 constexpr int NTHREADS = 256;
-constexpr int RING = 128;      // bias ring elements per query row
-constexpr int VT_STRIDE = BN + 4;  // V^T row: 34 dwords, conflict-free 8-byte reads
+constexpr int RROW = 3 * BN;   // bias ring row: [odd-slot mirror | even slot | odd slot]
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float NEG_INIT = -1.0e30f;  // finite start of the running max (log2 units)
@@ -60,11 +67,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// XOR swizzles of the 16-byte chunks of a row.  K: chunk ^ (row mod CHUNKS)
+// keeps the 32 rows an MFMA operand read touches on distinct banks.  V: a
+// transposing read touches 4 consecutive rows x 2..4 consecutive chunks, which
+// the per-row pattern below spreads over distinct banks.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int row) {
+  if constexpr (D == 128) {
+    constexpr int tab = (0) | (6 << 4) | (12 << 8) | (10 << 12);
+    return (tab >> ((row & 3) * 4)) & 15;
+  } else {
+    return 2 * (row & 3);
+  }
+}
+
 template <int D>
 struct __align__(16) PrefillSmem {
-  uint16_t k[BN * D];           // K tile, 16-byte chunks XOR-swizzled by key
-  uint16_t vt[D * VT_STRIDE];   // V^T tile
-  uint16_t ring[BM * RING];     // bias ring
+  uint16_t k[BN * D];           // K tile [key][D]
+  uint16_t v[BN * D];           // V tile [key][D]
+  uint16_t ring[BM * RROW];     // bias ring, one row per query
 };
 
 template <int D, bool BIG_PAGE, bool VEC_BIAS>
@@ -143,8 +164,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- K/V tile loaders (every load unconditional; rows past the end of
   // the sequence are read from inside the same page, then zeroed) ----------
   const int kc = tid % CHUNKS;          // 16-byte chunk this thread moves
-  const int krow0 = tid / CHUNKS;       // K rows krow0 + j*(NTHREADS/CHUNKS)
-  const int vkey0 = (tid / CHUNKS) * KPT;  // V keys vkey0 .. vkey0+KPT-1
+  const int krow0 = tid / CHUNKS;       // K and V rows krow0 + j*(NTHREADS/CHUNKS)
 
   u32x4_t kreg[KPT], vreg[KPT];
   const u32x4_t zero4 = {0, 0, 0, 0};
@@ -159,7 +179,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       for (int j = 0; j < KPT; ++j) {
         const int kr = krow0 + j * (NTHREADS / CHUNKS);
         kreg[j] = *reinterpret_cast<const u32x4_t *>(kt + (uint32_t)(kr * D + kc * 8));
-        vreg[j] = *reinterpret_cast<const u32x4_t *>(vt + (uint32_t)((vkey0 + j) * D + kc * 8));
+        vreg[j] = *reinterpret_cast<const u32x4_t *>(vt + (uint32_t)(kr * D + kc * 8));
       }
     } else {
 #pragma unroll
@@ -169,10 +189,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         const size_t ko = (size_t)trow[sk >> lp] * page_stride + (size_t)kvh * head_stride +
                           (size_t)(sk & (P - 1)) * D + kc * 8;
         kreg[j] = *reinterpret_cast<const u32x4_t *>(kp + ko);
-        const int sv = min(s0 + vkey0 + j, L - 1);
-        const size_t vo = (size_t)trow[sv >> lp] * page_stride + (size_t)kvh * head_stride +
-                          (size_t)(sv & (P - 1)) * D + kc * 8;
-        vreg[j] = *reinterpret_cast<const u32x4_t *>(vp + vo);
+        vreg[j] = *reinterpret_cast<const u32x4_t *>(vp + ko);
       }
     }
   };
@@ -183,32 +200,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int kr = krow0 + j * (NTHREADS / CHUNKS);
-      const int phys = kc ^ (kr & (CHUNKS - 1));
-      *reinterpret_cast<u32x4_t *>(&sm.k[kr * D + phys * 8]) = (s0 + kr < L) ? kreg[j] : zero4;
-      vreg[j] = (s0 + vkey0 + j < L) ? vreg[j] : zero4;
-    }
-    // V^T: element (key, d) -> vt[d][key]; this thread holds keys
-    // vkey0..vkey0+KPT-1 of head-dim chunk kc.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const int d = kc * 8 + e;
-      if constexpr (KPT == 4) {
-        u32x2_t pk;
-        pk[0] = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
-        pk[1] = ((vreg[2][w] >> sh) & 0xffffu) | (((vreg[3][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2_t *>(&sm.vt[d * VT_STRIDE + vkey0]) = pk;
-      } else {
-        const uint32_t pk = ((vreg[0][w] >> sh) & 0xffffu) | (((vreg[1][w] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint32_t *>(&sm.vt[d * VT_STRIDE + vkey0]) = pk;
-      }
+      const bool ok = s0 + kr < L;
+      *reinterpret_cast<u32x4_t *>(&sm.k[kr * D + ((kc ^ (kr & (CHUNKS - 1))) * 8)]) = ok ? kreg[j] : zero4;
+      *reinterpret_cast<u32x4_t *>(&sm.v[kr * D + ((kc ^ v_swizzle<D>(kr)) * 8)]) = ok ? vreg[j] : zero4;
     }
   };
 
   // ---- bias ring loader: one 64-wide distance chunk per query row ----------
   // For key tile s0, row q needs distances t0+q-s0-63 .. t0+q-s0, i.e. the
   // chunks lo(q) = floor((t0-s0-63+q)/64) and lo(q)+1.  Moving to the next
-  // tile (s0 += 64) needs chunk lo-1 and drops lo+1: same ring slot.
+  // tile (s0 += 64) needs chunk lo-1 and drops lo+1: same ring slot.  The
+  // ring row is [odd slot mirror | even slot | odd slot]: distance d lives at
+  // 64 + (d mod 128), and also at d mod 128 - 64 when its chunk is odd.
   // Thread tid moves 16-byte piece (tid & 7) of rows tid/8 + 32*j.
   u32x4_t breg[4];
   const int bq0 = tid >> 3;
@@ -247,7 +250,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       const int q = bq0 + 32 * j;
       const int e = chunk_elem(s0, q, which);
       const bool ok = (t0 + q < L) && e >= 0 && e < R;
-      *reinterpret_cast<u32x4_t *>(&sm.ring[q * RING + (e & (RING - 1))]) = ok ? breg[j] : zero4;
+      const u32x4_t v = ok ? breg[j] : zero4;
+      const int pos = BN + (e & (2 * BN - 1));
+      *reinterpret_cast<u32x4_t *>(&sm.ring[q * RROW + pos]) = v;
+      if (e & BN) *reinterpret_cast<u32x4_t *>(&sm.ring[q * RROW + pos - 2 * BN]) = v;
     }
   };
 
@@ -260,6 +266,24 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   float m2 = NEG_INIT;   // running max, log2 units, shared by the lane pair
   float lsum = 0.f;      // this lane's share of the softmax denominator
   const float scale = a.sm_scale;
+  const float scale2 = scale * LOG2E;
+
+  // ---- LDS read addressing ---------------------------------------------------
+  // K operand: lane reads key row col (+32 for the second key block), chunk
+  // (2kb + half) ^ (col mod CHUNKS) = (2kb) ^ kx.
+  const int kx = half ^ (col & (CHUNKS - 1));
+  const uint16_t *kbase = &sm.k[col * D];
+  // V operand via the transposing read: this lane supplies the address of
+  // key ks*16 + 4*(g/2) + kk (+8 for k-slots 4..7), head-dim elements
+  // ds*32 + 16*(g%2) + 4*i .. +3, where g = lane/16, kk = (lane/4)%4, i = lane%4.
+  // The read hands lane 16g+4i+j element j of lanes 16g+i+4kk, kk = 0..3, which
+  // is row d = ds*32 + lane%32 of V^T at keys ks*16 + 4*half + 0..3 (+8).
+  const int vg = lane >> 4, vkk = (lane >> 2) & 3, vi = lane & 3;
+  const int vrow = 4 * (vg >> 1) + vkk;
+  const int vchunk_lo = 2 * (vg & 1) + (vi >> 1);        // chunk within a 32-wide slab
+  const int vsw = v_swizzle<D>(vrow);                   // rows ks*16+vrow(+8) share it
+  const uint16_t *vbase = &sm.v[vrow * D + (vi & 1) * 4];
+  const uint16_t *ringrow = &sm.ring[q_local * RROW + BN];   // distance d at [d mod 128]
 
   auto compute_tile = [&](int s0) {
     const int tq0 = t0 + wave * 32;
@@ -269,118 +293,114 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     if (W > 0 && dmin_w >= W) return;          // every key lies before the window
     const bool need_mask = (dmin_w < 0) || (W > 0 && dmax_w >= W) || (s0 + BN > L);
     const bool band = dmin_w < R - 1;
+    // some visible distance beyond R-1 inside a band tile (global layers only)
+    const bool straddle = band && dmax_w > R - 1 && (W <= 0 || W > R);
+    // score path: 0 clamp-only unmasked, 1 band unmasked, 2 general
+    const int path = (!need_mask && !band) ? 0 : ((!need_mask && !straddle) ? 1 : 2);
+    // exp2 argument = fma(v, sa, sb - m2): v is the raw q.k on path 0 (scale
+    // and the clamped bias folded into sa, sb), the finished score otherwise
+    const float sa = (path == 0) ? scale2 : LOG2E;
+    const float sb = (path == 0) ? b_last * LOG2E : 0.f;
 
-    // S^T = K Q^T : two 32x32 blocks of keys x queries; K fragments are read
-    // from LDS one k-step ahead of the MFMAs that consume them
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[sub][j] = 0.f;
-    const int kbase0 = col * D;                // key row s0 + col; sub 1 adds 32 rows
-    const int ksw = col & (CHUNKS - 1);        // (32 + col) & (CHUNKS-1) is the same
-    // 2*KB fragments (k-step kb, sub-block sub) streamed one ahead of the MFMAs
-    auto kfrag = [&](int step) {
-      const int kb = step >> 1, sub = step & 1;
-      return *reinterpret_cast<const u32x4_t *>(
-          &sm.k[kbase0 + sub * 32 * D + (((2 * kb + half) ^ ksw) * 8)]);
-    };
-    u32x4_t kf[2];
-    kf[0] = kfrag(0);
-#pragma unroll
-    for (int step = 0; step < 2 * KB; ++step) {
-      if (step + 1 < 2 * KB) kf[(step + 1) & 1] = kfrag(step + 1);
-      const int kb = step >> 1, sub = step & 1;
-      sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[step & 1]),
-                                                          __builtin_bit_cast(bf16x8_t, qf[kb]), sacc[sub], 0, 0, 0);
-    }
-
-    // scores: scale, bias, mask.  A key at offset koff = key - s0 - 4*half
-    // from this lane's first key is visible iff kv_lo < koff <= kv_hi; the
-    // band/clamp choice is hoisted out of the element loop.
-    float mx = -INFINITY;
+    // The tile is processed as two 32-key halves (sub = 0, 1): S^T = K Q^T on
+    // one 32x32 block, its softmax update, then O^T += V^T P^T for its keys.
     const int dq = t - s0 - 4 * half;          // distance of key s0 + 4*half
-    int kv_hi = min(dq, L - 1 - s0 - 4 * half);
-    int kv_lo = (W > 0) ? dq - W : -1000000;
-    if (!need_mask) { kv_hi = 1000000; kv_lo = -1000000; }
-    const uint16_t *ringrow = &sm.ring[q_local * RING];
-    auto scores = [&](auto band_c) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x16_t sacc;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int koff = sub * 32 + 8 * (j >> 2) + (j & 3);   // key - s0 - 4*half
-          float bv = b_last;
-          if constexpr (decltype(band_c)::value) {
-            const int d = dq - koff;
-            const float ringv = bf16_to_f32(ringrow[d & (RING - 1)]);
-            bv = (d < R - 1) ? ringv : b_last;
+      for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+      const uint16_t *kb0 = kbase + sub * 32 * D;
+      u32x4_t kf[2];
+      kf[0] = *reinterpret_cast<const u32x4_t *>(kb0 + (kx * 8));
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (kb + 1 < KB)
+          kf[(kb + 1) & 1] = *reinterpret_cast<const u32x4_t *>(kb0 + (((2 * (kb + 1)) ^ kx) * 8));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb & 1]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[kb]), sacc, 0, 0, 0);
+      }
+
+      // Element j is key s0 + 4*half + koff, koff = 32*sub + 8*(j>>2) + (j&3),
+      // at distance dq - koff.  Four consecutive j share one ring base.
+      auto ring_group = [&](int g) {           // address of distance (dq - koff0 - 3)
+        const int d0 = dq - (32 * sub + 8 * g);
+        return ringrow + ((d0 & (2 * BN - 1)) - 3);
+      };
+      if (path == 1) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint16_t *rg = ring_group(g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sacc[4 * g + i] = fmaf(sacc[4 * g + i], scale, bf16_to_f32(rg[3 - i]));
+        }
+      } else if (path == 2) {
+        const int kv_hi = min(dq, L - 1 - s0 - 4 * half);   // visible iff kv_lo < koff <= kv_hi
+        const int kv_lo = (W > 0) ? dq - W : -1000000;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint16_t *rg = ring_group(g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int koff = 32 * sub + 8 * g + i;
+            const float bv = (band && dq - koff < R - 1) ? bf16_to_f32(rg[3 - i]) : b_last;
+            const float x = fmaf(sacc[4 * g + i], scale, bv);
+            sacc[4 * g + i] = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
           }
-          float x = fmaf(sacc[sub][j], scale, bv);
-          x = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
-          sacc[sub][j] = x;
         }
       }
-    };
-    if (band) scores(std::true_type{}); else scores(std::false_type{});
-    {
-      float m8[8];
+      {
+        float m4[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        m8[i] = fmaxf(fmaxf(sacc[i >> 2][(i & 3) * 4 + 0], sacc[i >> 2][(i & 3) * 4 + 1]),
-                      fmaxf(sacc[i >> 2][(i & 3) * 4 + 2], sacc[i >> 2][(i & 3) * 4 + 3]));
-      mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                 fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-    // online softmax with lazy rescaling
-    const float mt2 = mx * LOG2E;
-    const bool exceed = mt2 > m2 + TAU;
-    if (__ballot(exceed)) {
-      const float mnew = exceed ? mt2 : m2;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-      lsum *= alpha;
+        for (int i = 0; i < 4; ++i)
+          m4[i] = fmaxf(fmaxf(sacc[4 * i + 0], sacc[4 * i + 1]), fmaxf(sacc[4 * i + 2], sacc[4 * i + 3]));
+        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mt2 = fmaf(mx, sa, sb);
+        const bool exceed = mt2 > m2 + TAU;
+        if (__ballot(exceed)) {
+          const float mnew = exceed ? mt2 : m2;
+          const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+          lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < DSUB; ++i)
+          for (int i = 0; i < DSUB; ++i)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
-      m2 = mnew;
-    }
-    {
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+            for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
+          m2 = mnew;
+        }
+        const float c2 = sb - m2;
+        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[sub][j], LOG2E, -m2));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], sa, c2));
           ps[j & 3] += p;
-          sacc[sub][j] = p;
+          sacc[j] = p;
         }
-      lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    }
-
-    // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` are keys
-    // ks*16 + 4*half + {0,1,2,3,8,9,10,11}: exactly S^T registers 8*(ks&1)+0..7.
-    const uint16_t *vtrow = &sm.vt[col * VT_STRIDE + 4 * half];
-#pragma unroll
-    for (int ks = 0; ks < BN / 16; ++ks) {
-      const int sub = ks >> 1, rb = (ks & 1) * 8;
-      u32x4_t vw[DSUB];
-#pragma unroll
-      for (int ds = 0; ds < DSUB; ++ds) {
-        const uint16_t *vr = vtrow + ds * 32 * VT_STRIDE + ks * 16;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 8);
-        vw[ds] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       }
-      u32x4_t pw;
+
+      // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` are keys
+      // ks*16 + 4*half + {0,1,2,3,8,9,10,11}: exactly S^T registers 8*(ks&1)+0..7,
+      // and exactly the keys the two transposing reads deliver.
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(sacc[sub][rb + 2 * j], sacc[sub][rb + 2 * j + 1]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+      for (int kh = 0; kh < 2; ++kh) {
+        const int ks = 2 * sub + kh, rb = kh * 8;
+        u32x4_t pw;
 #pragma unroll
-      for (int ds = 0; ds < DSUB; ++ds)
-        oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vw[ds]), pb, oacc[ds], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(sacc[rb + 2 * j], sacc[rb + 2 * j + 1]);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+#pragma unroll
+        for (int ds = 0; ds < DSUB; ++ds) {
+          const uint16_t *v0 = vbase + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0 + 8 * D));
+          const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], hw[0], hw[1]});
+          oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pb, oacc[ds], 0, 0, 0);
+        }
+      }
     }
   };
 

@@ -130,19 +130,25 @@ def test_window_one_returns_value_exactly():
 
 
 def test_row_constant_bias_shift():
-    """Adding a constant to a whole bias row changes nothing beyond rounding."""
+    """Adding a constant to a whole bias row leaves the output unchanged.
+
+    The bias is drawn on a 1/16 grid in [-2, 2] and shifted by integers in
+    [-4, 4], so both the original and the shifted rows are exact in bf16 and
+    the two problems have the same exact answer."""
     dev = device()
     sp = spec(4, 2, 128, 0, 128, 64)
     case = ri.make_prefill(sp, [300], seed=17, device=dev, num_pages=5)
-    c = torch.randint(-4, 5, (300, 4, 1), device=dev).to(torch.bfloat16)
-    bias2 = (case.bias.float() + c.float()).to(torch.bfloat16)
-    case2 = ri.PrefillCase(**{**case.__dict__, "bias": bias2})
-    o1 = gpu_prefill(case)
+    grid = (case.bias.float() * 16).round().clamp(-32, 32) / 16
+    case1 = ri.PrefillCase(**{**case.__dict__, "bias": grid.to(torch.bfloat16)})
+    c = torch.randint(-4, 5, (300, 4, 1), device=dev).float()
+    shifted = (grid + c).to(torch.bfloat16)
+    assert torch.equal(shifted.float(), grid + c)
+    case2 = ri.PrefillCase(**{**case.__dict__, "bias": shifted})
+    o1 = gpu_prefill(case1)
     o2 = gpu_prefill(case2)
-    ref2 = oracle_prefill(case2)
-    assert_parity(o2, ref2, torch.bfloat16, "shifted")
+    assert_parity(o1, oracle_prefill(case1), torch.bfloat16, "grid bias")
+    assert_parity(o2, oracle_prefill(case2), torch.bfloat16, "shifted")
     max_abs, _ = errors(o1, o2.double().cpu().numpy())
-    # the shifted bias is itself rounded to bf16, so rows may move by rounding
     assert max_abs <= 2e-2
 
 
