@@ -246,7 +246,26 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline sample")
+    ap.add_argument("--copy-calibration-gib", type=int, default=0,
+                    help="only run a plain device copy of this many GiB, three times "
+                         "(the known-size kernel that scales FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+
+    if args.copy_calibration_gib > 0:
+        import torch
+        n = args.copy_calibration_gib << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 3
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 4,
+                          "read_plus_write_GBps": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
