@@ -11,19 +11,23 @@
 // on _build_rel_logits.
 //
 // Work decomposition (one work-group = 4 waves = 128 queries of one head):
-//  * 64-key K and V tiles are staged HBM -> registers (one tile ahead) ->
-//    LDS, both row-major with XOR-swizzled 16-byte chunks;
+//  * 64-key K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4,
+//    no register staging) into two buffers, row-major with XOR-swizzled
+//    16-byte chunks: tile i+1 streams in while tile i computes, one barrier
+//    per tile.  Rows past the end of a sequence are filled from its last key
+//    (finite data whose probabilities are exactly zero);
 //  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16, so each
 //    lane owns one query column: the softmax row statistics stay in a lane
 //    pair (lane, lane^32);
+//  * the K operand reads key rows in an order with bits 2 and 3 of the row
+//    index swapped, which hands each lane runs of 8 consecutive keys;
 //  * the V^T operand comes straight from the row-major V tile through the
 //    transposing LDS read ds_read_b64_tr_b16;
-//  * the bias of query row t at distance d sits in a per-row ring of two
-//    64-wide distance chunks in LDS, with the odd chunk mirrored in front of
-//    the even one so any four consecutive distances are contiguous; each key
-//    tile brings in one new chunk per row, loaded with aligned 16-byte reads,
-//    so every bias element crosses HBM once.  Tiles whose distances all lie
-//    at or beyond R-1 use the single clamped value bias[t,h,R-1];
+//  * the bias never touches LDS: for each tile a lane needs 32 distances of
+//    its own query row, four runs of 8 consecutive distances, which it loads
+//    as four 16-byte global reads (one tile ahead), so every bias element
+//    crosses HBM once.  Tiles whose distances all lie at or beyond R-1 use
+//    the single clamped value bias[t,h,R-1] and load nothing;
 //  * three score paths chosen per wave and tile: clamp-only unmasked (scale,
 //    bias and max folded into one FMA before exp2), band unmasked, and a
 //    general path for window/causal/sequence-end edges and the clamp border;
@@ -46,9 +50,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int BM = 128;        // queries per work-group
-constexpr int BN = 64;         // keys per tile (= one bias chunk)
+constexpr int BN = 64;         // keys per tile
 constexpr int NTHREADS = 256;
-constexpr int RROW = 3 * BN;   // bias ring row: [odd-slot mirror | even slot | odd slot]
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float NEG_INIT = -1.0e30f;  // finite start of the running max (log2 units)
@@ -56,6 +59,12 @@ constexpr float TAU = 8.0f;           // lazy-rescale threshold (log2 units)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
+}
+
+// Element e (compile-time) of eight packed bf16 values, as fp32.
+__device__ __forceinline__ float bf16x8_elem(const u32x4_t &p, int e) {
+  const uint32_t w = p[e >> 1];
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -69,8 +78,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // XOR swizzles of the 16-byte chunks of a row.  K: chunk ^ (row mod CHUNKS)
 // keeps the 32 rows an MFMA operand read touches on distinct banks.  V: a
-// transposing read touches 4 consecutive rows x 2..4 consecutive chunks, which
-// the per-row pattern below spreads over distinct banks.
+// transposing read touches 4 rows of equal (row mod 4) pattern x 2..4
+// consecutive chunks, which the per-row pattern below spreads over distinct
+// banks.
 template <int D>
 __device__ __forceinline__ int v_swizzle(int row) {
   if constexpr (D == 128) {
@@ -81,20 +91,32 @@ __device__ __forceinline__ int v_swizzle(int row) {
   }
 }
 
-template <int D>
-struct __align__(16) PrefillSmem {
-  uint16_t k[BN * D];           // K tile [key][D]
-  uint16_t v[BN * D];           // V tile [key][D]
-  uint16_t ring[BM * RROW];     // bias ring, one row per query
-};
+// Key row of S^T row m within a 32-key block: bits 2 and 3 swapped.  Lane
+// (col, half) then holds keys 8*half + 0..7 and 16 + 8*half + 0..7.
+__device__ __forceinline__ int key_of_row(int m) {
+  return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte-per-lane direct load: lane l's 16 bytes at src land at
+// lds + 16*l.  (Kept in a device function of its own: the host compilation
+// pass drops kernels that name this builtin directly.)
+__device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
+  __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
 
 template <int D, bool BIG_PAGE, bool VEC_BIAS>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
-  constexpr int KPT = BN * CHUNKS / NTHREADS;   // key rows per thread per tile
   constexpr int KB = D / 16;                    // MFMA k-steps over head_dim
   constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
-  __shared__ PrefillSmem<D> sm;
+  constexpr int ROWS_PER_DMA = 512 / D;         // key rows per 1 KiB LDS write
+  constexpr int DMA_PER_WAVE = BN * D / 2048;   // 1 KiB writes per wave per matrix
+  // two K/V buffers as separate objects, so the compiler can tell that the
+  // direct loads into one do not alias reads of the other
+  __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
+  __shared__ __align__(16) uint16_t k_lds1[BN * D], v_lds1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,10 +162,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int lp = a.log2_page;
   const size_t head_stride = (size_t)P * D;           // elements per (page, head)
   const size_t page_stride = (size_t)a.Hkv * head_stride;
-  // bias rows of this work-group start here; row q adds q * Hq * R
-  const uint16_t *bwg = static_cast<const uint16_t *>(a.bias) +
-                        ((size_t)(tok0 + t0) * Hq + h) * R;
-  const uint32_t brow_stride = (uint32_t)Hq * (uint32_t)R;
 
   // ---- this lane's query row --------------------------------------------
   const int col = lane & 31;
@@ -159,101 +177,88 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     const u32x4_t v = *reinterpret_cast<const u32x4_t *>(qp + row * D + kb * 16 + half * 8);
     qf[kb] = row_ok ? v : u32x4_t{0, 0, 0, 0};
   }
-  const float b_last = bf16_to_f32(bwg[(row_ok ? (uint32_t)q_local : 0u) * brow_stride + (R - 1)]);
 
-  // ---- K/V tile loaders (every load unconditional; rows past the end of
-  // the sequence are read from inside the same page, then zeroed) ----------
-  const int kc = tid % CHUNKS;          // 16-byte chunk this thread moves
-  const int krow0 = tid / CHUNKS;       // K and V rows krow0 + j*(NTHREADS/CHUNKS)
+  // Bias row of this lane's query.  A tile a wave reads bias for has every
+  // distance of the wave inside [-94, R + 94), so 16-byte runs read at those
+  // offsets stay inside the bias tensor except for rows within 1024 elements
+  // of either end of it: waves holding such a row read element by element
+  // with distances clamped to [0, R) instead.  Values read outside [0, R)
+  // are masked or replaced by the clamped bucket.
+  const uint16_t *brow = static_cast<const uint16_t *>(a.bias) + row * R;
+  const float b_last = bf16_to_f32(brow[R - 1]);
+  const long long row_off = (long long)row * R;
+  const long long bias_elems = (long long)a.total_tokens * Hq * R;
+  const bool edge_wave = __ballot(row_off < 1024 || bias_elems - row_off < R + 1024) != 0;
 
-  u32x4_t kreg[KPT], vreg[KPT];
+  // ---- K/V tile loads, global -> LDS -------------------------------------
+  // Write j of this wave fills LDS rows (DMA_PER_WAVE*wave + j)*ROWS_PER_DMA
+  // + lane/CHUNKS, physical chunk lane%CHUNKS, which holds logical chunk
+  // (lane%CHUNKS) ^ swizzle(row) of the key row.
   const u32x4_t zero4 = {0, 0, 0, 0};
-
-  auto load_kv = [&](int s0) {
-    if constexpr (BIG_PAGE) {
-      const int page = trow[s0 >> lp];
-      const uint16_t *kt = kp + (size_t)page * page_stride + (size_t)kvh * head_stride +
-                           (size_t)(s0 & (P - 1)) * D;
-      const uint16_t *vt = vp + (kt - kp);
+  int dma_row[DMA_PER_WAVE];            // tile row this lane fills, per write
+  uint32_t k_off[DMA_PER_WAVE], v_off[DMA_PER_WAVE];   // byte offset inside the row
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int kr = krow0 + j * (NTHREADS / CHUNKS);
-        kreg[j] = *reinterpret_cast<const u32x4_t *>(kt + (uint32_t)(kr * D + kc * 8));
-        vreg[j] = *reinterpret_cast<const u32x4_t *>(vt + (uint32_t)(kr * D + kc * 8));
+  for (int j = 0; j < DMA_PER_WAVE; ++j) {
+    const int rw = (DMA_PER_WAVE * wave + j) * ROWS_PER_DMA + lane / CHUNKS;
+    const int pc = lane % CHUNKS;
+    dma_row[j] = rw;
+    k_off[j] = (uint32_t)((pc ^ (rw & (CHUNKS - 1))) * 16);
+    v_off[j] = (uint32_t)((pc ^ v_swizzle<D>(rw)) * 16);
+  }
+
+  // `page` is the pool page of the tile when pages hold whole tiles; it is
+  // read from the block table one tile ahead of its use, so the table read
+  // never sits in front of the tile's loads.
+  auto load_kv = [&](int s0, int page_v, uint16_t *kl, uint16_t *vl) {
+    const int last = L - 1 - s0;        // rows above this repeat the last key
+    if constexpr (BIG_PAGE) {
+      // the 64-key tile lies inside one page
+      const int page = __builtin_amdgcn_readfirstlane(page_v);
+      const char *kt = reinterpret_cast<const char *>(
+          kp + (size_t)page * page_stride + (size_t)kvh * head_stride + (size_t)(s0 & (P - 1)) * D);
+      const char *vt = reinterpret_cast<const char *>(vp) + (kt - reinterpret_cast<const char *>(kp));
+#pragma unroll
+      for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const uint32_t ro = (uint32_t)min(dma_row[j], last) * (D * 2);
+        lds_void_t *kd = (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512);
+        lds_void_t *vd = (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512);
+        dma16(kt + (ro + k_off[j]), kd);
+        dma16(vt + (ro + v_off[j]), vd);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int kr = krow0 + j * (NTHREADS / CHUNKS);
-        const int sk = min(s0 + kr, L - 1);
-        const size_t ko = (size_t)trow[sk >> lp] * page_stride + (size_t)kvh * head_stride +
-                          (size_t)(sk & (P - 1)) * D + kc * 8;
-        kreg[j] = *reinterpret_cast<const u32x4_t *>(kp + ko);
-        vreg[j] = *reinterpret_cast<const u32x4_t *>(vp + ko);
+      for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const int sk = s0 + min(dma_row[j], last);
+        const size_t ko = ((size_t)trow[sk >> lp] * page_stride + (size_t)kvh * head_stride +
+                           (size_t)(sk & (P - 1)) * D) * 2;
+        lds_void_t *kd = (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512);
+        lds_void_t *vd = (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512);
+        dma16(reinterpret_cast<const char *>(kp) + ko + k_off[j], kd);
+        dma16(reinterpret_cast<const char *>(vp) + ko + v_off[j], vd);
       }
     }
   };
 
-  // Rows at or past the end of the sequence are zeroed here, at the LDS
-  // write, so the loads themselves stay unconditional and in flight.
-  auto commit_kv = [&](int s0) {
+  // ---- bias runs ---------------------------------------------------------
+  // For key tile s0, run p (p = 2*sub + G) holds the distances
+  // t - s0 - 8*half - 16*p - 7 .. t - s0 - 8*half - 16*p in ascending order,
+  // i.e. the keys s0 + 32*sub + 16*G + 8*half + 7 down to + 0.
+  auto load_bias = [&](int s0, u32x4_t (&bp)[4]) {
+    const int ds0 = t - s0 - 8 * half - 7;
+    if (VEC_BIAS && !edge_wave) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int kr = krow0 + j * (NTHREADS / CHUNKS);
-      const bool ok = s0 + kr < L;
-      *reinterpret_cast<u32x4_t *>(&sm.k[kr * D + ((kc ^ (kr & (CHUNKS - 1))) * 8)]) = ok ? kreg[j] : zero4;
-      *reinterpret_cast<u32x4_t *>(&sm.v[kr * D + ((kc ^ v_swizzle<D>(kr)) * 8)]) = ok ? vreg[j] : zero4;
-    }
-  };
-
-  // ---- bias ring loader: one 64-wide distance chunk per query row ----------
-  // For key tile s0, row q needs distances t0+q-s0-63 .. t0+q-s0, i.e. the
-  // chunks lo(q) = floor((t0-s0-63+q)/64) and lo(q)+1.  Moving to the next
-  // tile (s0 += 64) needs chunk lo-1 and drops lo+1: same ring slot.  The
-  // ring row is [odd slot mirror | even slot | odd slot]: distance d lives at
-  // 64 + (d mod 128), and also at d mod 128 - 64 when its chunk is odd.
-  // Thread tid moves 16-byte piece (tid & 7) of rows tid/8 + 32*j.
-  u32x4_t breg[4];
-  const int bq0 = tid >> 3;
-  const int bv8 = (tid & 7) * 8;
-
-  auto chunk_elem = [&](int s0, int q, int which) {
-    return (((t0 - s0 - (BN - 1) + q) >> 6) + which) * BN + bv8;
-  };
-
-  auto load_chunk = [&](int s0, int which) {
+      for (int p = 0; p < 4; ++p) __builtin_memcpy(&bp[p], brow + (ds0 - 16 * p), 16);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = bq0 + 32 * j;
-      const int e = chunk_elem(s0, q, which);
-      const bool ok = (t0 + q < L) && e >= 0 && e < R;
-      if constexpr (VEC_BIAS) {
-        const uint32_t off = ok ? (uint32_t)q * brow_stride + (uint32_t)e : 0u;
-        breg[j] = *reinterpret_cast<const u32x4_t *>(bwg + off);
-      } else {
+      for (int p = 0; p < 4; ++p) {
         u32x4_t v = zero4;
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const bool okx = ok && (e + x < R);
-          const uint32_t off = okx ? (uint32_t)q * brow_stride + (uint32_t)(e + x) : 0u;
-          const uint32_t el = bwg[off];
-          v[x >> 1] |= (okx ? el : 0u) << ((x & 1) * 16);
+          const int d = min(max(ds0 - 16 * p + x, 0), R - 1);
+          v[x >> 1] |= (uint32_t)brow[d] << ((x & 1) * 16);
         }
-        breg[j] = v;
+        bp[p] = v;
       }
-    }
-  };
-
-  auto commit_chunk = [&](int s0, int which) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = bq0 + 32 * j;
-      const int e = chunk_elem(s0, q, which);
-      const bool ok = (t0 + q < L) && e >= 0 && e < R;
-      const u32x4_t v = ok ? breg[j] : zero4;
-      const int pos = BN + (e & (2 * BN - 1));
-      *reinterpret_cast<u32x4_t *>(&sm.ring[q * RROW + pos]) = v;
-      if (e & BN) *reinterpret_cast<u32x4_t *>(&sm.ring[q * RROW + pos - 2 * BN]) = v;
     }
   };
 
@@ -269,23 +274,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const float scale2 = scale * LOG2E;
 
   // ---- LDS read addressing ---------------------------------------------------
-  // K operand: lane reads key row col (+32 for the second key block), chunk
-  // (2kb + half) ^ (col mod CHUNKS) = (2kb) ^ kx.
-  const int kx = half ^ (col & (CHUNKS - 1));
-  const uint16_t *kbase = &sm.k[col * D];
+  // K operand: lane supplies S^T row col = key key_of_row(col) (+32 for the
+  // second key block), chunk (2kb + half) ^ (key mod CHUNKS) = (2kb) ^ kx.
+  const int krow = key_of_row(col);
+  const int kx = half ^ (krow & (CHUNKS - 1));
+  const int kbase = krow * D;
   // V operand via the transposing read: this lane supplies the address of
-  // key ks*16 + 4*(g/2) + kk (+8 for k-slots 4..7), head-dim elements
+  // key ks*16 + 8*(g/2) + kk (+4 for k-slots 4..7), head-dim elements
   // ds*32 + 16*(g%2) + 4*i .. +3, where g = lane/16, kk = (lane/4)%4, i = lane%4.
   // The read hands lane 16g+4i+j element j of lanes 16g+i+4kk, kk = 0..3, which
-  // is row d = ds*32 + lane%32 of V^T at keys ks*16 + 4*half + 0..3 (+8).
+  // is row d = ds*32 + lane%32 of V^T at keys ks*16 + 8*half + 0..3 (+4).
   const int vg = lane >> 4, vkk = (lane >> 2) & 3, vi = lane & 3;
-  const int vrow = 4 * (vg >> 1) + vkk;
+  const int vrow = 8 * (vg >> 1) + vkk;
   const int vchunk_lo = 2 * (vg & 1) + (vi >> 1);        // chunk within a 32-wide slab
-  const int vsw = v_swizzle<D>(vrow);                   // rows ks*16+vrow(+8) share it
-  const uint16_t *vbase = &sm.v[vrow * D + (vi & 1) * 4];
-  const uint16_t *ringrow = &sm.ring[q_local * RROW + BN];   // distance d at [d mod 128]
+  const int vsw = v_swizzle<D>(vrow);                   // rows ks*16+vrow(+4) share it
+  const int vbase = vrow * D + (vi & 1) * 4;
 
-  auto compute_tile = [&](int s0) {
+  auto compute_tile = [&](int s0, const uint16_t *kl, const uint16_t *vl, const u32x4_t (&bp)[4]) {
     const int tq0 = t0 + wave * 32;
     const int dmax_w = tq0 + 31 - s0;
     const int dmin_w = tq0 - (s0 + BN - 1);
@@ -302,15 +307,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     const float sa = (path == 0) ? scale2 : LOG2E;
     const float sb = (path == 0) ? b_last * LOG2E : 0.f;
 
-    // The tile is processed as two 32-key halves (sub = 0, 1): S^T = K Q^T on
-    // one 32x32 block, its softmax update, then O^T += V^T P^T for its keys.
-    const int dq = t - s0 - 4 * half;          // distance of key s0 + 4*half
+    // Element j of 32-key half `sub` is key s0 + 8*half + koff,
+    // koff = 32*sub + 16*(j>>3) + (j&7), at distance dq - koff.
+    const int dq = t - s0 - 8 * half;
+
+    const uint16_t *kt = kl + kbase;
+    const uint16_t *vt = vl + vbase;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       f32x16_t sacc;
 #pragma unroll
       for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
-      const uint16_t *kb0 = kbase + sub * 32 * D;
+      const uint16_t *kb0 = kt + sub * 32 * D;
       u32x4_t kf[2];
       kf[0] = *reinterpret_cast<const u32x4_t *>(kb0 + (kx * 8));
 #pragma unroll
@@ -321,33 +329,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
                                                        __builtin_bit_cast(bf16x8_t, qf[kb]), sacc, 0, 0, 0);
       }
 
-      // Element j is key s0 + 4*half + koff, koff = 32*sub + 8*(j>>2) + (j&3),
-      // at distance dq - koff.  Four consecutive j share one ring base.
-      auto ring_group = [&](int g) {           // address of distance (dq - koff0 - 3)
-        const int d0 = dq - (32 * sub + 8 * g);
-        return ringrow + ((d0 & (2 * BN - 1)) - 3);
-      };
       if (path == 1) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint16_t *rg = ring_group(g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sacc[4 * g + i] = fmaf(sacc[4 * g + i], scale, bf16_to_f32(rg[3 - i]));
-        }
+        for (int j = 0; j < 16; ++j)
+          sacc[j] = fmaf(sacc[j], scale, bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)));
       } else if (path == 2) {
-        const int kv_hi = min(dq, L - 1 - s0 - 4 * half);   // visible iff kv_lo < koff <= kv_hi
+        const int kv_hi = min(dq, L - 1 - s0 - 8 * half);   // visible iff kv_lo < koff <= kv_hi
         const int kv_lo = (W > 0) ? dq - W : -1000000;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint16_t *rg = ring_group(g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int koff = 32 * sub + 8 * g + i;
-            const float bv = (band && dq - koff < R - 1) ? bf16_to_f32(rg[3 - i]) : b_last;
-            const float x = fmaf(sacc[4 * g + i], scale, bv);
-            sacc[4 * g + i] = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
-          }
+        for (int j = 0; j < 16; ++j) {
+          const int koff = 32 * sub + 16 * (j >> 3) + (j & 7);
+          const float bv = (band && dq - koff < R - 1)
+                               ? bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)) : b_last;
+          const float x = fmaf(sacc[j], scale, bv);
+          sacc[j] = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
         }
       }
       {
@@ -380,9 +375,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       }
 
-      // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` are keys
-      // ks*16 + 4*half + {0,1,2,3,8,9,10,11}: exactly S^T registers 8*(ks&1)+0..7,
-      // and exactly the keys the two transposing reads deliver.
+      // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` in
+      // step ks are keys ks*16 + 8*half + 0..7: exactly S^T registers
+      // 8*(ks&1) + 0..7, and exactly the keys the two transposing reads deliver.
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks = 2 * sub + kh, rb = kh * 8;
@@ -392,9 +387,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
         const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
         for (int ds = 0; ds < DSUB; ++ds) {
-          const uint16_t *v0 = vbase + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
+          const uint16_t *v0 = vt + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0 + 8 * D));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0 + 4 * D));
           const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
           const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
           const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], hw[0], hw[1]});
@@ -404,44 +399,57 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
     }
   };
 
-  // ---- main loop: prefetch tile i+1 while computing tile i -----------------
-  auto wg_band = [&](int s0) { return t0 - (s0 + BN - 1) < R - 1; };
+  // ---- main loop -------------------------------------------------------------
+  // Tile i computes from buffer i%2 while tile i+1's K/V stream into the
+  // other buffer and its bias runs into the other register set; the barrier
+  // closing tile i waits for both.  Unrolled by two so each buffer and each
+  // register set is fixed at compile time.
+  auto wave_band = [&](int s0) {      // this wave computes tile s0 and reads its bias
+    const int tq0 = t0 + wave * 32;
+    const int dmin_w = tq0 - (s0 + BN - 1);
+    return (tq0 + 31 - s0 >= 0) && !(W > 0 && dmin_w >= W) && dmin_w < R - 1;
+  };
 
-  load_kv(s_begin);
-  bool ring_ready = false;
-  const bool band0 = wg_band(s_begin);
-  if (band0) load_chunk(s_begin, 0);
-  commit_kv(s_begin);
-  if (band0) {
-    commit_chunk(s_begin, 0);
-    load_chunk(s_begin, 1);
-    commit_chunk(s_begin, 1);
-    ring_ready = true;
-  }
+  u32x4_t bias0[4] = {zero4, zero4, zero4, zero4};
+  u32x4_t bias1[4] = {zero4, zero4, zero4, zero4};
+  // Page of tile s (0 past the last tile, where it is not used).  The index
+  // carries an opaque zero so the value stays in a vector register until
+  // load_kv reads it, instead of being moved to a scalar register (and
+  // waited for) right after the load.
+  const int opaque_zero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);   // 0 in every lane
+  auto tile_page = [&](int s) {
+    return BIG_PAGE && s <= t_last ? trow[(s >> lp) + opaque_zero] : 0;
+  };
+  load_kv(s_begin, tile_page(s_begin), k_lds0, v_lds0);
+  if (wave_band(s_begin)) load_bias(s_begin, bias0);
+  int page_next = tile_page(s_begin + BN);
   __syncthreads();
 
-  for (int s0 = s_begin; s0 <= t_last; s0 += BN) {
-    const int sn = s0 + BN;
-    const bool has_next = sn <= t_last;
-    const bool band_next = has_next && wg_band(sn);
-    if (has_next) {
-      load_kv(sn);
-      if (band_next) load_chunk(sn, 0);
-    }
-    compute_tile(s0);
-    __syncthreads();
-    if (has_next) {
-      commit_kv(sn);
-      if (band_next) {
-        commit_chunk(sn, 0);
-        if (!ring_ready) {
-          load_chunk(sn, 1);
-          commit_chunk(sn, 1);
-          ring_ready = true;
-        }
+  for (int s0 = s_begin;;) {
+    {
+      const int sn = s0 + BN;
+      if (sn <= t_last) {
+        load_kv(sn, page_next, k_lds1, v_lds1);
+        if (wave_band(sn)) load_bias(sn, bias1);
+        page_next = tile_page(sn + BN);
       }
+      compute_tile(s0, k_lds0, v_lds0, bias0);
+      __syncthreads();
+      if (sn > t_last) break;
+      s0 = sn;
     }
-    __syncthreads();
+    {
+      const int sn = s0 + BN;
+      if (sn <= t_last) {
+        load_kv(sn, page_next, k_lds0, v_lds0);
+        if (wave_band(sn)) load_bias(sn, bias0);
+        page_next = tile_page(sn + BN);
+      }
+      compute_tile(s0, k_lds1, v_lds1, bias1);
+      __syncthreads();
+      if (sn > t_last) break;
+      s0 = sn;
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -469,7 +477,7 @@ template <int D>
 static void launch_d(const PrefillArgs &a, hipStream_t s) {
   dim3 grid(a.num_blocks), block(NTHREADS);
   const bool big = a.page_size >= BN;
-  const bool vec = (a.R & 7) == 0;
+  const bool vec = a.R >= 8;
   if (big && vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, s, a);
   else if (big) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, s, a);
   else if (vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, s, a);

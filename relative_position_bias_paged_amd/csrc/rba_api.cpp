@@ -151,6 +151,7 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
   a.log2_page = ilog2(pt->page_size);
   a.window = params->window > 0 ? params->window : 0;
   a.R = params->rel_extent;
+  a.total_tokens = total_tokens;
   a.sm_scale = params->sm_scale;
 
   hipError_t err;

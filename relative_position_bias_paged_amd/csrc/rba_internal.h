@@ -19,6 +19,7 @@ struct PrefillArgs {
   float *lse;                // [T][Hq] or null
   int32_t num_seqs, Hq, Hkv, G, max_pages, page_size, log2_page;
   int32_t window, R;
+  int32_t total_tokens;      // T: rows of q, out and bias
   int32_t num_qtiles;        // query tiles per (sequence, head)
   int32_t num_blocks;        // total work-groups of the launch
   float sm_scale;
