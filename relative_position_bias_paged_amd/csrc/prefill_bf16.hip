@@ -365,14 +365,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
           m2 = mnew;
         }
         const float c2 = sb - m2;
-        float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[j], sa, c2));
-          ps[j & 3] += p;
-          sacc[j] = p;
+        for (int j = 0; j < 16; ++j) sacc[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], sa, c2));
+      }
+      // P in bf16, as the PV MFMA consumes it; the row sum adds exactly these
+      // rounded values, two per v_dot2 against (1, 1).
+      u32x4_t pw[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pw[j >> 2][j & 3] = pack_bf16x2(sacc[2 * j], sacc[2 * j + 1]);
+      {
+        const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // (bit_cast of a vector element lvalue reads element 0: copy it out first)
+          const uint32_t w0 = pw[0][j], w1 = pw[1][j];
+          s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), one2, s0, false);
+          s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), one2, s1, false);
         }
-        lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        lsum += s0 + s1;
       }
 
       // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` in
@@ -380,11 +391,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
       // 8*(ks&1) + 0..7, and exactly the keys the two transposing reads deliver.
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const int ks = 2 * sub + kh, rb = kh * 8;
-        u32x4_t pw;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pw[j] = pack_bf16x2(sacc[rb + 2 * j], sacc[rb + 2 * j + 1]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+        const int ks = 2 * sub + kh;
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw[kh]);
 #pragma unroll
         for (int ds = 0; ds < DSUB; ++ds) {
           const uint16_t *v0 = vt + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
