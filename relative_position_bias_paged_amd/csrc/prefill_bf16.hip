@@ -23,11 +23,14 @@
 //    index swapped, which hands each lane runs of 8 consecutive keys;
 //  * the V^T operand comes straight from the row-major V tile through the
 //    transposing LDS read ds_read_b64_tr_b16;
-//  * the bias never touches LDS: for each tile a lane needs 32 distances of
-//    its own query row, four runs of 8 consecutive distances, which it loads
-//    as four 16-byte global reads (one tile ahead), so every bias element
-//    crosses HBM once.  Tiles whose distances all lie at or beyond R-1 use
-//    the single clamped value bias[t,h,R-1] and load nothing;
+//  * for each tile a query row needs the 64 distances t-s0-63 .. t-s0 of its
+//    bias row.  Each wave streams them for its 32 rows straight into a 4 KiB
+//    LDS stage of its own (global_load_lds_dwordx4, eight lanes per row, so
+//    a load instruction touches 8 rows instead of 32), one tile ahead, and
+//    every lane then picks its four runs of 8 consecutive distances out of
+//    it with aligned 16-byte reads; every bias element crosses HBM once.
+//    Tiles whose distances all lie at or beyond R-1 use the single clamped
+//    value bias[t,h,R-1] and load nothing;
 //  * three score paths chosen per wave and tile: clamp-only unmasked (scale,
 //    bias and max folded into one FMA before exp2), band unmasked, and a
 //    general path for window/causal/sequence-end edges and the clamp border;
@@ -106,6 +109,10 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8) that waits for LDS and scalar memory traffic only.
+constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
+
 template <int D, bool BIG_PAGE, bool VEC_BIAS>
 __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
@@ -117,6 +124,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // direct loads into one do not alias reads of the other
   __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
   __shared__ __align__(16) uint16_t k_lds1[BN * D], v_lds1[BN * D];
+  // bias stage: per wave, 32 rows x 64 distances, 16-byte chunks of row r
+  // XOR-swizzled by (r/2) mod 8 so the lanes' aligned reads avoid bank conflicts
+  __shared__ __align__(16) uint16_t bias_stage[4 * 32 * BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,11 +189,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   }
 
   // Bias row of this lane's query.  A tile a wave reads bias for has every
-  // distance of the wave inside [-94, R + 94), so 16-byte runs read at those
-  // offsets stay inside the bias tensor except for rows within 1024 elements
-  // of either end of it: waves holding such a row read element by element
-  // with distances clamped to [0, R) instead.  Values read outside [0, R)
-  // are masked or replaced by the clamped bucket.
+  // distance of the wave inside [-94, R + 94), so the staged 64-distance rows
+  // stay inside the bias tensor except for rows within 1024 elements of
+  // either end of it: waves holding such a row read element by element with
+  // distances clamped to [0, R) instead.  Values read outside [0, R) are
+  // masked or replaced by the clamped bucket.
   const uint16_t *brow = static_cast<const uint16_t *>(a.bias) + row * R;
   const float b_last = bf16_to_f32(brow[R - 1]);
   const long long row_off = (long long)row * R;
@@ -242,13 +252,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- bias runs ---------------------------------------------------------
   // For key tile s0, run p (p = 2*sub + G) holds the distances
   // t - s0 - 8*half - 16*p - 7 .. t - s0 - 8*half - 16*p in ascending order,
-  // i.e. the keys s0 + 32*sub + 16*G + 8*half + 7 down to + 0.
-  auto load_bias = [&](int s0, u32x4_t (&bp)[4]) {
-    const int ds0 = t - s0 - 8 * half - 7;
-    if (VEC_BIAS && !edge_wave) {
+  // i.e. the keys s0 + 32*sub + 16*G + 8*half + 7 down to + 0: chunk
+  // 7 - half - 2p of the row's 64 staged distances t - s0 - 63 .. t - s0.
+  const bool use_stage = VEC_BIAS && !edge_wave;
+  uint16_t *stage_w = bias_stage + wave * (32 * BN);
+  // Stage write k of this lane: row 8k + lane/8 of the wave, physical chunk
+  // lane%8 = logical chunk c ^ swizzle.  Pointer for tile 0; tile s0 is
+  // s0 elements lower.
+  const char *sptr[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) __builtin_memcpy(&bp[p], brow + (ds0 - 16 * p), 16);
+  for (int k = 0; k < 4; ++k) {
+    const int rq = 8 * k + (lane >> 3);
+    const int tq = t0 + wave * 32 + rq;
+    const int c = (lane & 7) ^ ((rq >> 1) & 7);
+    const size_t rrow = ((size_t)tok0 + (tq < L ? tq : 0)) * Hq + h;
+    sptr[k] = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.bias) + rrow * R) +
+              2 * (long long)(tq - (BN - 1) + 8 * c);
+  }
+  auto stage_bias = [&](int s0) {       // direct loads, tile s0 -> this wave's stage
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dma16(sptr[k] - 2 * (long long)s0, (lds_void_t *)(stage_w + k * 512));
+  };
+  auto load_bias = [&](int s0, u32x4_t (&bp)[4]) {
+    if (use_stage) {
+      const int sw = (col >> 1) & 7;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        bp[p] = *reinterpret_cast<const u32x4_t *>(stage_w + col * BN + (((7 - half - 2 * p) ^ sw) * 8));
     } else {
+      const int ds0 = t - s0 - 8 * half - 7;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         u32x4_t v = zero4;
@@ -408,18 +440,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   };
 
   // ---- main loop -------------------------------------------------------------
-  // Tile i computes from buffer i%2 while tile i+1's K/V stream into the
-  // other buffer and its bias runs into the other register set; the barrier
-  // closing tile i waits for both.  Unrolled by two so each buffer and each
-  // register set is fixed at compile time.
+  // Tile i computes from K/V buffer i%2 while tile i+1's K/V stream into the
+  // other buffer and its bias rows into the wave's stage (after the lanes
+  // have copied tile i's runs out of it); the barrier closing tile i waits
+  // for both.  Unrolled by two so each buffer is fixed at compile time.
   auto wave_band = [&](int s0) {      // this wave computes tile s0 and reads its bias
     const int tq0 = t0 + wave * 32;
     const int dmin_w = tq0 - (s0 + BN - 1);
     return (tq0 + 31 - s0 >= 0) && !(W > 0 && dmin_w >= W) && dmin_w < R - 1;
   };
 
-  u32x4_t bias0[4] = {zero4, zero4, zero4, zero4};
-  u32x4_t bias1[4] = {zero4, zero4, zero4, zero4};
+  u32x4_t bias_r[4] = {zero4, zero4, zero4, zero4};
   // Page of tile s (0 past the last tile, where it is not used).  The index
   // carries an opaque zero so the value stays in a vector register until
   // load_kv reads it, instead of being moved to a scalar register (and
@@ -428,36 +459,33 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   auto tile_page = [&](int s) {
     return BIG_PAGE && s <= t_last ? trow[(s >> lp) + opaque_zero] : 0;
   };
+  // One tile: bias runs of tile s0 into registers, then the loads of tile
+  // sn = s0 + BN, then the compute of tile s0.
+  auto step = [&](int s0, uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, int &page_next) {
+    const int sn = s0 + BN;
+    if (wave_band(s0)) load_bias(s0, bias_r);
+    if (sn <= t_last) {
+      load_kv(sn, page_next, kn, vn);
+      page_next = tile_page(sn + BN);
+      if (use_stage && wave_band(sn)) {
+        // the stage is rewritten: this lane's reads of it must be done
+        __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
+        stage_bias(sn);
+      }
+    }
+    compute_tile(s0, kc, vc, bias_r);
+    __syncthreads();
+    return sn <= t_last;
+  };
+
   load_kv(s_begin, tile_page(s_begin), k_lds0, v_lds0);
-  if (wave_band(s_begin)) load_bias(s_begin, bias0);
+  if (use_stage && wave_band(s_begin)) stage_bias(s_begin);
   int page_next = tile_page(s_begin + BN);
   __syncthreads();
 
-  for (int s0 = s_begin;;) {
-    {
-      const int sn = s0 + BN;
-      if (sn <= t_last) {
-        load_kv(sn, page_next, k_lds1, v_lds1);
-        if (wave_band(sn)) load_bias(sn, bias1);
-        page_next = tile_page(sn + BN);
-      }
-      compute_tile(s0, k_lds0, v_lds0, bias0);
-      __syncthreads();
-      if (sn > t_last) break;
-      s0 = sn;
-    }
-    {
-      const int sn = s0 + BN;
-      if (sn <= t_last) {
-        load_kv(sn, page_next, k_lds0, v_lds0);
-        if (wave_band(sn)) load_bias(sn, bias0);
-        page_next = tile_page(sn + BN);
-      }
-      compute_tile(s0, k_lds1, v_lds1, bias1);
-      __syncthreads();
-      if (sn > t_last) break;
-      s0 = sn;
-    }
+  for (int s0 = s_begin;; s0 += 2 * BN) {
+    if (!step(s0, k_lds0, v_lds0, k_lds1, v_lds1, page_next)) break;
+    if (!step(s0 + BN, k_lds1, v_lds1, k_lds0, v_lds0, page_next)) break;
   }
 
   // ---- epilogue ------------------------------------------------------------
