@@ -10,7 +10,10 @@
 // its [T, heads, rel_extent] shape is the one in that page's review comment
 // on _build_rel_logits.
 //
-// Work decomposition (one work-group = 4 waves = 128 queries of one head):
+// Work decomposition: a work-group of NW waves (4 or 8) covers hpw query
+// heads of one KV head times NW/hpw blocks of 32 consecutive queries; each
+// wave owns 32 queries of one head and every K/V tile it loads serves all
+// 32*NW (head, query) rows:
 //  * 64-key K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4,
 //    no register staging) into two buffers, row-major with XOR-swizzled
 //    16-byte chunks: tile i+1 streams in while tile i computes, one barrier
@@ -52,9 +55,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int BM = 128;        // queries per work-group
 constexpr int BN = 64;         // keys per tile
-constexpr int NTHREADS = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float NEG_INIT = -1.0e30f;  // finite start of the running max (log2 units)
@@ -113,29 +114,29 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
 // 11:8) that waits for LDS and scalar memory traffic only.
 constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
 
-template <int D, bool BIG_PAGE, bool VEC_BIAS>
-__global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a) {
+template <int D, int NW, bool BIG_PAGE, bool VEC_BIAS>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
   constexpr int KB = D / 16;                    // MFMA k-steps over head_dim
   constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
   constexpr int ROWS_PER_DMA = 512 / D;         // key rows per 1 KiB LDS write
-  constexpr int DMA_PER_WAVE = BN * D / 2048;   // 1 KiB writes per wave per matrix
+  constexpr int DMA_PER_WAVE = BN * D / 512 / NW;  // 1 KiB writes per wave per matrix
   // two K/V buffers as separate objects, so the compiler can tell that the
   // direct loads into one do not alias reads of the other
   __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
   __shared__ __align__(16) uint16_t k_lds1[BN * D], v_lds1[BN * D];
   // bias stage: per wave, 32 rows x 64 distances, 16-byte chunks of row r
   // XOR-swizzled by (r/2) mod 8 so the lanes' aligned reads avoid bank conflicts
-  __shared__ __align__(16) uint16_t bias_stage[4 * 32 * BN];
+  __shared__ __align__(16) uint16_t bias_stage[NW * 32 * BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
 
-  // Work-group -> (sequence, head, query tile).  Blocks are dealt to the 8
-  // XCDs round-robin; remap so each XCD walks a contiguous range, in which
-  // the query heads of one KV head and its query tiles (heaviest first)
-  // are adjacent and share that XCD's L2.
+  // Work-group -> (sequence, KV head, head group, query tile).  Blocks are
+  // dealt to the 8 XCDs round-robin; remap so each XCD walks a contiguous
+  // range, in which the head groups of one KV head and its query tiles
+  // (heaviest first) are adjacent and share that XCD's L2.
   const int nb = a.num_blocks;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, xidx = bid >> 3;
@@ -143,24 +144,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int r = (xcd < rem) ? xcd * (base + 1) + xidx
                             : rem * (base + 1) + (xcd - rem) * base + xidx;
   const int nqt = a.num_qtiles;
-  const int per_seq = a.Hq * nqt;
+  const int hpw = a.hpw;                     // query heads per work-group
+  const int ngroups = a.G / hpw;             // head groups per KV head
+  const int per_seq = a.Hkv * ngroups * nqt;
   const int b = r / per_seq;
   int rr = r - b * per_seq;
-  const int per_kvh = a.G * nqt;
+  const int per_kvh = ngroups * nqt;
   const int kvh = rr / per_kvh;
   rr -= kvh * per_kvh;
-  const int qt = nqt - 1 - rr / a.G;
-  const int h = kvh * a.G + rr % a.G;
+  const int qt = nqt - 1 - rr / ngroups;
+  const int hg = rr % ngroups;
+  const int QM = 32 * (NW / hpw);            // queries per head per work-group
+  // this wave: head slot wave % hpw, query block wave / hpw
+  const int h = kvh * a.G + hg * hpw + wave % hpw;
+  const int qb = wave / hpw;
 
   const int tok0 = a.cu_seqlens[b];
   const int L = a.cu_seqlens[b + 1] - tok0;
-  const int t0 = qt * BM;
+  const int t0 = qt * QM;
   if (t0 >= L) return;
+  const int tq0 = t0 + 32 * qb;              // this wave's first query
 
   const int Hq = a.Hq;
   const int R = a.R;
   const int W = a.window;
-  const int t_last = min(t0 + BM, L) - 1;
+  const int t_last = min(t0 + QM, L) - 1;
   int s_begin = (W > 0) ? max(0, t0 - W + 1) : 0;
   s_begin &= ~(BN - 1);
 
@@ -176,8 +184,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // ---- this lane's query row --------------------------------------------
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int q_local = wave * 32 + col;
-  const int t = t0 + q_local;
+  const int t = tq0 + col;
   const bool row_ok = t < L;
   const size_t row = ((size_t)tok0 + (row_ok ? t : 0)) * Hq + h;
 
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int rq = 8 * k + (lane >> 3);
-    const int tq = t0 + wave * 32 + rq;
+    const int tq = tq0 + rq;
     const int c = (lane & 7) ^ ((rq >> 1) & 7);
     const size_t rrow = ((size_t)tok0 + (tq < L ? tq : 0)) * Hq + h;
     sptr[k] = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.bias) + rrow * R) +
@@ -323,7 +330,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   const int vbase = vrow * D + (vi & 1) * 4;
 
   auto compute_tile = [&](int s0, const uint16_t *kl, const uint16_t *vl, const u32x4_t (&bp)[4]) {
-    const int tq0 = t0 + wave * 32;
     const int dmax_w = tq0 + 31 - s0;
     const int dmin_w = tq0 - (s0 + BN - 1);
     if (dmax_w < 0) return;                    // every key lies in this wave's future
@@ -445,7 +451,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
   // have copied tile i's runs out of it); the barrier closing tile i waits
   // for both.  Unrolled by two so each buffer is fixed at compile time.
   auto wave_band = [&](int s0) {      // this wave computes tile s0 and reads its bias
-    const int tq0 = t0 + wave * 32;
     const int dmin_w = tq0 - (s0 + BN - 1);
     return (tq0 + 31 - s0 >= 0) && !(W > 0 && dmin_w >= W) && dmin_w < R - 1;
   };
@@ -509,22 +514,25 @@ __global__ __launch_bounds__(NTHREADS, 2) void prefill_bf16_kernel(PrefillArgs a
 
 }  // namespace
 
-template <int D>
+template <int D, int NW>
 static void launch_d(const PrefillArgs &a, hipStream_t s) {
-  dim3 grid(a.num_blocks), block(NTHREADS);
+  dim3 grid(a.num_blocks), block(64 * NW);
   const bool big = a.page_size >= BN;
   const bool vec = a.R >= 8;
-  if (big && vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), grid, block, 0, s, a);
-  else if (big) hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, s, a);
-  else if (vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, s, a);
+  if (big && vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, true>), grid, block, 0, s, a);
+  else if (big) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, false>), grid, block, 0, s, a);
+  else if (vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, false>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
+  if (a.waves != 4 && a.waves != 8) return hipErrorInvalidValue;
   if (head_dim == 128) {
-    launch_d<128>(a, s);
+    if (a.waves == 8) launch_d<128, 8>(a, s);
+    else launch_d<128, 4>(a, s);
   } else if (head_dim == 64) {
-    launch_d<64>(a, s);
+    if (a.waves == 8) launch_d<64, 8>(a, s);
+    else launch_d<64, 4>(a, s);
   } else {
     return hipErrorInvalidValue;
   }

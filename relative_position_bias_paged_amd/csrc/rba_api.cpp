@@ -15,7 +15,14 @@
 
 namespace {
 
-constexpr int kPrefillBM = 128;      // queries per bf16 prefill work-group
+// Waves per bf16 prefill work-group on local (windowed) and global layers.
+// Every K/V tile a work-group loads serves 32 (head, query) rows per wave.
+#ifndef RBA_PREFILL_WAVES_LOCAL
+#define RBA_PREFILL_WAVES_LOCAL 4
+#endif
+#ifndef RBA_PREFILL_WAVES_GLOBAL
+#define RBA_PREFILL_WAVES_GLOBAL 8
+#endif
 constexpr int kF32Rows = 64;         // queries per fp32 prefill work-group
 constexpr int kMaxSplits = 256;
 constexpr int kAutoChunkPages = 32;  // automatic partitions hold about this many pages
@@ -156,8 +163,14 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
 
   hipError_t err;
   if (kv->dtype == RBA_BF16) {
-    a.num_qtiles = (max_seqlen + kPrefillBM - 1) / kPrefillBM;
-    const long long blocks = (long long)a.num_seqs * a.Hq * a.num_qtiles;
+    // Query heads of one KV head share a work-group (and its K/V tiles):
+    // the largest of 8, 4, 2, 1 that divides both G and the wave count.
+    a.waves = a.window > 0 ? RBA_PREFILL_WAVES_LOCAL : RBA_PREFILL_WAVES_GLOBAL;
+    a.hpw = 1;
+    while (a.hpw * 2 <= a.waves && a.G % (a.hpw * 2) == 0) a.hpw *= 2;
+    const int qm = 32 * (a.waves / a.hpw);       // queries per head per work-group
+    a.num_qtiles = (max_seqlen + qm - 1) / qm;
+    const long long blocks = (long long)a.num_seqs * a.Hkv * (a.G / a.hpw) * a.num_qtiles;
     if (blocks > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
     a.num_blocks = (int32_t)blocks;
     err = rba::launch_prefill_bf16(a, kv->head_dim, stream);

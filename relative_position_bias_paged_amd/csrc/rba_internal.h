@@ -20,7 +20,9 @@ struct PrefillArgs {
   int32_t num_seqs, Hq, Hkv, G, max_pages, page_size, log2_page;
   int32_t window, R;
   int32_t total_tokens;      // T: rows of q, out and bias
-  int32_t num_qtiles;        // query tiles per (sequence, head)
+  int32_t waves;             // waves per work-group (bf16 kernel: 4 or 8)
+  int32_t hpw;               // query heads per work-group (divides G and waves)
+  int32_t num_qtiles;        // query tiles per (sequence, head group)
   int32_t num_blocks;        // total work-groups of the launch
   float sm_scale;
 };
