@@ -351,11 +351,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
 
     const uint16_t *kt = kl + kbase;
     const uint16_t *vt = vl + vbase;
+
+    // S^T block of keys 32*sub .. 32*sub+31 (8 MFMAs over head_dim).
+    auto s_block = [&](int sub) {
+      f32x16_t acc;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16_t sacc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) sacc[j] = 0.f;
+      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
       const uint16_t *kb0 = kt + sub * 32 * D;
       u32x4_t kf[2];
       kf[0] = *reinterpret_cast<const u32x4_t *>(kb0 + (kx * 8));
@@ -363,14 +364,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       for (int kb = 0; kb < KB; ++kb) {
         if (kb + 1 < KB)
           kf[(kb + 1) & 1] = *reinterpret_cast<const u32x4_t *>(kb0 + (((2 * (kb + 1)) ^ kx) * 8));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb & 1]),
-                                                       __builtin_bit_cast(bf16x8_t, qf[kb]), sacc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb & 1]),
+                                                      __builtin_bit_cast(bf16x8_t, qf[kb]), acc, 0, 0, 0);
       }
-
+      return acc;
+    };
+    // Finished scores of a block on paths 1 and 2 (path 0 keeps the raw q.k).
+    auto finish = [&](f32x16_t &acc, int sub) {
       if (path == 1) {
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          sacc[j] = fmaf(sacc[j], scale, bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)));
+          acc[j] = fmaf(acc[j], scale, bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)));
       } else if (path == 2) {
         const int kv_hi = min(dq, L - 1 - s0 - 8 * half);   // visible iff kv_lo < koff <= kv_hi
         const int kv_lo = (W > 0) ? dq - W : -1000000;
@@ -379,54 +383,41 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
           const int koff = 32 * sub + 16 * (j >> 3) + (j & 7);
           const float bv = (band && dq - koff < R - 1)
                                ? bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)) : b_last;
-          const float x = fmaf(sacc[j], scale, bv);
-          sacc[j] = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
+          const float x = fmaf(acc[j], scale, bv);
+          acc[j] = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
         }
       }
-      {
-        float m4[4];
+    };
+    auto max16 = [&](const f32x16_t &acc) {
+      float m4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          m4[i] = fmaxf(fmaxf(sacc[4 * i + 0], sacc[4 * i + 1]), fmaxf(sacc[4 * i + 2], sacc[4 * i + 3]));
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mt2 = fmaf(mx, sa, sb);
-        const bool exceed = mt2 > m2 + TAU;
-        if (__ballot(exceed)) {
-          const float mnew = exceed ? mt2 : m2;
-          const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-          lsum *= alpha;
+      for (int i = 0; i < 4; ++i)
+        m4[i] = fmaxf(fmaxf(acc[4 * i + 0], acc[4 * i + 1]), fmaxf(acc[4 * i + 2], acc[4 * i + 3]));
+      return fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+    };
+    // P = exp2(score - max) in bf16, as the PV MFMA consumes it; the row sum
+    // adds exactly these rounded values, two per v_dot2 against (1, 1).
+    auto probs = [&](f32x16_t &acc, float c2, u32x4_t (&pw)[2]) {
 #pragma unroll
-          for (int i = 0; i < DSUB; ++i)
+      for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_exp2f(fmaf(acc[j], sa, c2));
 #pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
-          m2 = mnew;
-        }
-        const float c2 = sb - m2;
+      for (int j = 0; j < 8; ++j) pw[j >> 2][j & 3] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sacc[j] = __builtin_amdgcn_exp2f(fmaf(sacc[j], sa, c2));
+      for (int j = 0; j < 4; ++j) {
+        // (bit_cast of a vector element lvalue reads element 0: copy it out first)
+        const uint32_t w0 = pw[0][j], w1 = pw[1][j];
+        r0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), one2, r0, false);
+        r1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), one2, r1, false);
       }
-      // P in bf16, as the PV MFMA consumes it; the row sum adds exactly these
-      // rounded values, two per v_dot2 against (1, 1).
-      u32x4_t pw[2];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pw[j >> 2][j & 3] = pack_bf16x2(sacc[2 * j], sacc[2 * j + 1]);
-      {
-        const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // (bit_cast of a vector element lvalue reads element 0: copy it out first)
-          const uint32_t w0 = pw[0][j], w1 = pw[1][j];
-          s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), one2, s0, false);
-          s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), one2, s1, false);
-        }
-        lsum += s0 + s1;
-      }
-
-      // O^T += V^T P^T, 16 keys per MFMA.  k-slots of lane half `half` in
-      // step ks are keys ks*16 + 8*half + 0..7: exactly S^T registers
-      // 8*(ks&1) + 0..7, and exactly the keys the two transposing reads deliver.
+      lsum += r0 + r1;
+    };
+    // O^T += V^T P^T over keys 32*sub .. 32*sub+31, 16 keys per MFMA.  k-slots
+    // of lane half `half` in step ks are keys ks*16 + 8*half + 0..7: exactly
+    // S^T registers 8*(ks&1) + 0..7, and exactly the keys the two transposing
+    // reads deliver.
+    auto pv_block = [&](const u32x4_t (&pw)[2], int sub) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int ks = 2 * sub + kh;
@@ -442,7 +433,37 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
           oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pb, oacc[ds], 0, 0, 0);
         }
       }
+    };
+
+    // The two 32-key blocks are software-pipelined so that MFMA work of one
+    // block is in flight while the VALU works on the other: block 1's S^T
+    // MFMAs run during block 0's score finishing, block 0's PV MFMAs during
+    // block 1's exponentials.  The running max is updated once per tile.
+    f32x16_t sa0 = s_block(0);
+    f32x16_t sa1 = s_block(1);
+    finish(sa0, 0);
+    const float mx0 = max16(sa0);
+    finish(sa1, 1);
+    float mx = fmaxf(mx0, max16(sa1));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt2 = fmaf(mx, sa, sb);
+    const bool exceed = mt2 > m2 + TAU;
+    if (__ballot(exceed)) {
+      const float mnew = exceed ? mt2 : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DSUB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
+      m2 = mnew;
     }
+    const float c2 = sb - m2;
+    u32x4_t pw0[2], pw1[2];
+    probs(sa0, c2, pw0);
+    pv_block(pw0, 0);
+    probs(sa1, c2, pw1);
+    pv_block(pw1, 1);
   };
 
   // ---- main loop -------------------------------------------------------------
