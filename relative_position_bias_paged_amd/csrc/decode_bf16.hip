@@ -81,15 +81,21 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
 
+  // Block -> (partition, sequence, KV head, head group), partition slowest.
+  // Blocks are dealt to the 8 XCDs round-robin, so every XCD gets a mix of
+  // sequences at every partition index; with the partition fastest, a
+  // partition count that is a multiple of 8 would send partition j to XCD
+  // j mod 8 every time, and the late partitions (which exist only for long
+  // sequences) would leave some XCDs idle while others still work.
   const int S = a.num_splits;
   const int HG = a.head_groups;
   int item = blockIdx.x;
   const int hg = item % HG;
   item /= HG;
-  const int split = item % S;
-  item /= S;
   const int kvh = item % a.Hkv;
-  const int b = item / a.Hkv;
+  item /= a.Hkv;
+  const int b = item % a.num_seqs;
+  const int split = item / a.num_seqs;
 
   const int G = a.G;
   const int h_base = kvh * G + hg * 4;
