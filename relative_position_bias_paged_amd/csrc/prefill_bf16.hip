@@ -340,6 +340,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const bool straddle = band && dmax_w > R - 1 && (W <= 0 || W > R);
     // score path: 0 clamp-only unmasked, 1 band unmasked, 2 general
     const int path = (!need_mask && !band) ? 0 : ((!need_mask && !straddle) ? 1 : 2);
+    // no visible key of this wave lies beyond distance R-1 (a windowed layer
+    // with window <= R, or a band tile that does not reach R-1): the staged
+    // bias serves every key of a path-2 tile
+    const bool clamp_free = band && ((W > 0 && W <= R) || dmax_w < R);
     // exp2 argument = fma(v, sa, sb - m2): v is the raw q.k on path 0 (scale
     // and the clamped bias folded into sa, sb), the finished score otherwise
     const float sa = (path == 0) ? scale2 : LOG2E;
@@ -376,15 +380,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         for (int j = 0; j < 16; ++j)
           acc[j] = fmaf(acc[j], scale, bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)));
       } else if (path == 2) {
-        const int kv_hi = min(dq, L - 1 - s0 - 8 * half);   // visible iff kv_lo < koff <= kv_hi
-        const int kv_lo = (W > 0) ? dq - W : -1000000;
+        // visible iff kv_lo < koff <= kv_hi, i.e. (unsigned)(koff - kv_lo - 1) < span
+        const int kv_hi = min(dq, L - 1 - s0 - 8 * half);
+        const int kv_lo1 = (W > 0) ? dq - W + 1 : -(1 << 30);
+        const uint32_t span = (uint32_t)max(kv_hi - kv_lo1 + 1, 0);
+        if (clamp_free) {
+          // every visible distance is below R-1 or equals it (bias[R-1] = b_last)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int koff = 32 * sub + 16 * (j >> 3) + (j & 7);
-          const float bv = (band && dq - koff < R - 1)
-                               ? bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)) : b_last;
-          const float x = fmaf(acc[j], scale, bv);
-          acc[j] = (koff > kv_lo && koff <= kv_hi) ? x : -INFINITY;
+          for (int j = 0; j < 16; ++j) {
+            const int koff = 32 * sub + 16 * (j >> 3) + (j & 7);
+            const float x = fmaf(acc[j], scale, bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)));
+            acc[j] = ((uint32_t)(koff - kv_lo1) < span) ? x : -INFINITY;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int koff = 32 * sub + 16 * (j >> 3) + (j & 7);
+            const float bv = (band && dq - koff < R - 1)
+                                 ? bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)) : b_last;
+            const float x = fmaf(acc[j], scale, bv);
+            acc[j] = ((uint32_t)(koff - kv_lo1) < span) ? x : -INFINITY;
+          }
         }
       }
     };
