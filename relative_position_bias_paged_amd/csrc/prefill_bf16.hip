@@ -503,12 +503,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   };
   // One tile: bias runs of tile s0 into registers, then the loads of tile
   // sn = s0 + BN, then the compute of tile s0.
-  auto step = [&](int s0, uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, int &page_next) {
-    const int sn = s0 + BN;
+  // Key tiles T_first .. T_last of this work-group are visited in rotated
+  // order, tile index = step (mod n_t): on a windowed layer the interior
+  // work-groups of one head span the same number of tiles, so every
+  // work-group that needs a K/V tile loads it in the same step and the
+  // co-resident ones share it in L2.  (The online softmax does not depend on
+  // the order; on global layers T_first = 0 and the order is the natural one,
+  // which already aligns the work-groups.)
+  const int T_first = s_begin / BN;
+  const int n_t = t_last / BN - T_first + 1;
+  const int rot = (n_t - T_first % n_t) % n_t;
+  auto tile_s = [&](int k) {
+    int r = k + rot;
+    if (r >= n_t) r -= n_t;
+    return (T_first + r) * BN;
+  };
+  // One step k: bias runs of its tile into registers, then the loads of
+  // tile k+1, then the compute of tile k.
+  auto step = [&](int k, uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, int &page_next) {
+    const int s0 = tile_s(k);
+    const bool more = k + 1 < n_t;
     if (wave_band(s0)) load_bias(s0, bias_r);
-    if (sn <= t_last) {
+    if (more) {
+      const int sn = tile_s(k + 1);
       load_kv(sn, page_next, kn, vn);
-      page_next = tile_page(sn + BN);
+      page_next = (k + 2 < n_t) ? tile_page(tile_s(k + 2)) : 0;
       if (use_stage && wave_band(sn)) {
         // the stage is rewritten: this lane's reads of it must be done
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
@@ -517,17 +536,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     }
     compute_tile(s0, kc, vc, bias_r);
     __syncthreads();
-    return sn <= t_last;
+    return more;
   };
 
-  load_kv(s_begin, tile_page(s_begin), k_lds0, v_lds0);
-  if (use_stage && wave_band(s_begin)) stage_bias(s_begin);
-  int page_next = tile_page(s_begin + BN);
+  const int s_first = tile_s(0);
+  load_kv(s_first, tile_page(s_first), k_lds0, v_lds0);
+  if (use_stage && wave_band(s_first)) stage_bias(s_first);
+  int page_next = (n_t > 1) ? tile_page(tile_s(1)) : 0;
   __syncthreads();
 
-  for (int s0 = s_begin;; s0 += 2 * BN) {
-    if (!step(s0, k_lds0, v_lds0, k_lds1, v_lds1, page_next)) break;
-    if (!step(s0 + BN, k_lds1, v_lds1, k_lds0, v_lds0, page_next)) break;
+  for (int k = 0;; k += 2) {
+    if (!step(k, k_lds0, v_lds0, k_lds1, v_lds1, page_next)) break;
+    if (!step(k + 1, k_lds1, v_lds1, k_lds0, v_lds0, page_next)) break;
   }
 
   // ---- epilogue ------------------------------------------------------------
