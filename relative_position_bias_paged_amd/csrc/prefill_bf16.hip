@@ -43,6 +43,7 @@
 //    than 2^8), which is exact because numerator and denominator share it.
 #include "rba_internal.h"
 
+#include <climits>
 #include <type_traits>
 
 namespace rba {
@@ -172,6 +173,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   int s_begin = (W > 0) ? max(0, t0 - W + 1) : 0;
   s_begin &= ~(BN - 1);
 
+  // Key tile s0 (a multiple of BN) against this wave's queries tq0..tq0+31,
+  // each test one compare with a per-wave bound (d = t - s ranges over
+  // [tq0 - s0 - 63, tq0 + 31 - s0]):
+  //   active     s_lo < s0 <= s_hi  some key is visible
+  //   band       s0 > s_band        some distance is below R-1 (bias staged)
+  //   masked     s0 > s_diag, s0 <= s_wedge or s0 > s_tail
+  //              (causal diagonal, window edge, sequence end inside the tile)
+  //   beyond     s0 <= s_strad      some distance exceeds R-1
+  const int s_hi = tq0 + 31;
+  const int s_lo = (W > 0) ? tq0 - (BN - 1) - W : INT_MIN;
+  const int s_band = tq0 - (BN - 2) - R;
+  const int s_diag = tq0 - (BN - 1);
+  const int s_wedge = (W > 0) ? tq0 + 31 - W : INT_MIN;
+  const int s_tail = L - BN;
+  const int s_strad = tq0 + 31 - R;
+  // a layer whose window stays within the R buckets never sees a clamped
+  // distance inside its window
+  const bool wide_layer = W <= 0 || W > R;
+
   const uint16_t *qp = static_cast<const uint16_t *>(a.q);
   const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
   const uint16_t *vp = static_cast<const uint16_t *>(a.v_pool);
@@ -226,14 +246,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // `page` is the pool page of the tile when pages hold whole tiles; it is
   // read from the block table one tile ahead of its use, so the table read
   // never sits in front of the tile's loads.
+  const char *k_head = reinterpret_cast<const char *>(kp + (size_t)kvh * head_stride);
+  const long long v_minus_k = reinterpret_cast<const char *>(vp) - reinterpret_cast<const char *>(kp);
+  const uint32_t page_bytes = (uint32_t)(page_stride * 2);   // checked on the host to fit
   auto load_kv = [&](int s0, int page_v, uint16_t *kl, uint16_t *vl) {
     const int last = L - 1 - s0;        // rows above this repeat the last key
     if constexpr (BIG_PAGE) {
       // the 64-key tile lies inside one page
-      const int page = __builtin_amdgcn_readfirstlane(page_v);
-      const char *kt = reinterpret_cast<const char *>(
-          kp + (size_t)page * page_stride + (size_t)kvh * head_stride + (size_t)(s0 & (P - 1)) * D);
-      const char *vt = reinterpret_cast<const char *>(vp) + (kt - reinterpret_cast<const char *>(kp));
+      const uint32_t page = (uint32_t)__builtin_amdgcn_readfirstlane(page_v);
+      const char *kt = k_head + ((uint64_t)page * page_bytes + (uint32_t)((s0 & (P - 1)) * D * 2));
+      const char *vt = kt + v_minus_k;
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j) {
         const uint32_t ro = (uint32_t)min(dma_row[j], last) * (D * 2);
@@ -330,20 +352,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int vbase = vrow * D + (vi & 1) * 4;
 
   auto compute_tile = [&](int s0, const uint16_t *kl, const uint16_t *vl, const u32x4_t (&bp)[4]) {
-    const int dmax_w = tq0 + 31 - s0;
-    const int dmin_w = tq0 - (s0 + BN - 1);
-    if (dmax_w < 0) return;                    // every key lies in this wave's future
-    if (W > 0 && dmin_w >= W) return;          // every key lies before the window
-    const bool need_mask = (dmin_w < 0) || (W > 0 && dmax_w >= W) || (s0 + BN > L);
-    const bool band = dmin_w < R - 1;
-    // some visible distance beyond R-1 inside a band tile (global layers only)
-    const bool straddle = band && dmax_w > R - 1 && (W <= 0 || W > R);
-    // score path: 0 clamp-only unmasked, 1 band unmasked, 2 general
-    const int path = (!need_mask && !band) ? 0 : ((!need_mask && !straddle) ? 1 : 2);
+    if (s0 > s_hi || s0 <= s_lo) return;       // no key of the tile is visible to this wave
+    const bool need_mask = s0 > s_diag || s0 <= s_wedge || s0 > s_tail;
+    const bool band = s0 > s_band;
+    const bool beyond = s0 <= s_strad;         // some distance exceeds R-1
+    // score path: 0 clamp-only unmasked, 1 band unmasked, 2 general (a band
+    // tile with a visible distance beyond R-1 is one of the edges)
+    const int path = (!need_mask && !band) ? 0 : ((!need_mask && !(beyond && wide_layer)) ? 1 : 2);
     // no visible key of this wave lies beyond distance R-1 (a windowed layer
     // with window <= R, or a band tile that does not reach R-1): the staged
     // bias serves every key of a path-2 tile
-    const bool clamp_free = band && ((W > 0 && W <= R) || dmax_w < R);
+    const bool clamp_free = band && (!wide_layer || !beyond);
     // exp2 argument = fma(v, sa, sb - m2): v is the raw q.k on path 0 (scale
     // and the clamped bias folded into sa, sb), the finished score otherwise
     const float sa = (path == 0) ? scale2 : LOG2E;
@@ -460,12 +479,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     finish(sa0, 0);
     const float mx0 = max16(sa0);
     finish(sa1, 1);
-    float mx = fmaxf(mx0, max16(sa1));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt2 = fmaf(mx, sa, sb);
-    const bool exceed = mt2 > m2 + TAU;
-    if (__ballot(exceed)) {
-      const float mnew = exceed ? mt2 : m2;
+    // Lazy rescale, decided per lane on its own 32 scores: while neither lane
+    // of a pair sees a score above m2 + TAU the shared m2 stands, with no
+    // exchange; otherwise the pair's maximum is formed and both lanes move
+    // m2 to it.
+    const float mt2 = fmaf(fmaxf(mx0, max16(sa1)), sa, sb);
+    if (__ballot(mt2 > m2 + TAU)) {
+      const float mtp = fmaxf(mt2, __shfl_xor(mt2, 32));
+      const bool exceed = mtp > m2 + TAU;
+      const float mnew = exceed ? mtp : m2;
       const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
       lsum *= alpha;
 #pragma unroll
@@ -488,8 +510,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // have copied tile i's runs out of it); the barrier closing tile i waits
   // for both.  Unrolled by two so each buffer is fixed at compile time.
   auto wave_band = [&](int s0) {      // this wave computes tile s0 and reads its bias
-    const int dmin_w = tq0 - (s0 + BN - 1);
-    return (tq0 + 31 - s0 >= 0) && !(W > 0 && dmin_w >= W) && dmin_w < R - 1;
+    return s0 <= s_hi && s0 > s_lo && s0 > s_band;
   };
 
   u32x4_t bias_r[4] = {zero4, zero4, zero4, zero4};
@@ -498,8 +519,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // load_kv reads it, instead of being moved to a scalar register (and
   // waited for) right after the load.
   const int opaque_zero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);   // 0 in every lane
-  auto tile_page = [&](int s) {
-    return BIG_PAGE && s <= t_last ? trow[(s >> lp) + opaque_zero] : 0;
+  auto tile_page = [&](int s) {       // s is always a tile of this work-group
+    return BIG_PAGE ? trow[(s >> lp) + opaque_zero] : 0;
   };
   // One tile: bias runs of tile s0 into registers, then the loads of tile
   // sn = s0 + BN, then the compute of tile s0.
@@ -513,41 +534,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int T_first = s_begin / BN;
   const int n_t = t_last / BN - T_first + 1;
   const int rot = (n_t - T_first % n_t) % n_t;
-  auto tile_s = [&](int k) {
-    int r = k + rot;
-    if (r >= n_t) r -= n_t;
-    return (T_first + r) * BN;
-  };
-  // One step k: bias runs of its tile into registers, then the loads of
-  // tile k+1, then the compute of tile k.
-  auto step = [&](int k, uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, int &page_next) {
-    const int s0 = tile_s(k);
-    const bool more = k + 1 < n_t;
+  const int s_tfirst = T_first * BN, s_tlast = (T_first + n_t - 1) * BN;
+  auto tile_after = [&](int s) { return s == s_tlast ? s_tfirst : s + BN; };
+  // s_cur, s_nxt, s_nxt2: tiles of this step and the next two (the sequence
+  // wraps, so all three are always tiles of this work-group); page_nxt is
+  // the pool page of s_nxt, read one step ahead.
+  int s_cur = (T_first + rot) * BN;
+  int s_nxt = tile_after(s_cur);
+  int s_nxt2 = tile_after(s_nxt);
+  int steps_left = n_t;
+  // One step: bias runs of tile s_cur into registers, then the loads of
+  // s_nxt (unless s_cur is the last), then the compute of s_cur.
+  auto step = [&](uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, int &page_nxt) {
+    const int s0 = s_cur;
+    const bool more = --steps_left > 0;
     if (wave_band(s0)) load_bias(s0, bias_r);
     if (more) {
-      const int sn = tile_s(k + 1);
-      load_kv(sn, page_next, kn, vn);
-      page_next = (k + 2 < n_t) ? tile_page(tile_s(k + 2)) : 0;
-      if (use_stage && wave_band(sn)) {
+      load_kv(s_nxt, page_nxt, kn, vn);
+      page_nxt = tile_page(s_nxt2);
+      if (use_stage && wave_band(s_nxt)) {
         // the stage is rewritten: this lane's reads of it must be done
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
-        stage_bias(sn);
+        stage_bias(s_nxt);
       }
     }
     compute_tile(s0, kc, vc, bias_r);
     __syncthreads();
+    s_cur = s_nxt;
+    s_nxt = s_nxt2;
+    s_nxt2 = tile_after(s_nxt2);
     return more;
   };
 
-  const int s_first = tile_s(0);
-  load_kv(s_first, tile_page(s_first), k_lds0, v_lds0);
-  if (use_stage && wave_band(s_first)) stage_bias(s_first);
-  int page_next = (n_t > 1) ? tile_page(tile_s(1)) : 0;
+  load_kv(s_cur, tile_page(s_cur), k_lds0, v_lds0);
+  if (use_stage && wave_band(s_cur)) stage_bias(s_cur);
+  int page_nxt = tile_page(s_nxt);
   __syncthreads();
 
-  for (int k = 0;; k += 2) {
-    if (!step(k, k_lds0, v_lds0, k_lds1, v_lds1, page_next)) break;
-    if (!step(k + 1, k_lds1, v_lds1, k_lds0, v_lds0, page_next)) break;
+  for (;;) {
+    if (!step(k_lds0, v_lds0, k_lds1, v_lds1, page_nxt)) break;
+    if (!step(k_lds1, v_lds1, k_lds0, v_lds0, page_nxt)) break;
   }
 
   // ---- epilogue ------------------------------------------------------------

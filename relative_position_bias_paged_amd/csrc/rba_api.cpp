@@ -172,6 +172,8 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
     a.num_qtiles = (max_seqlen + qm - 1) / qm;
     const long long blocks = (long long)a.num_seqs * a.Hkv * (a.G / a.hpw) * a.num_qtiles;
     if (blocks > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
+    // the kernel forms page offsets as (32-bit page id) x (32-bit page bytes)
+    if ((long long)a.Hkv * a.page_size * kv->head_dim * 2 > 0xffffffffLL) return RBA_ERR_UNSUPPORTED;
     a.num_blocks = (int32_t)blocks;
     err = rba::launch_prefill_bf16(a, kv->head_dim, stream);
   } else {
