@@ -41,6 +41,19 @@ CASES = [
     ("r-odd-clamp", spec(4, 2, 128, 0, 37, 64), [300], 5),
     ("window1", spec(4, 2, 128, 1, 8, 64), [150], 3),
     ("empty-and-single", spec(4, 2, 128, 0, 64, 64), [0, 1, 65, 0, 2], 8),
+    # head groupings of the work-group: 4 and 8 query heads per KV head share
+    # one work-group (32 queries per head), 3 query heads share none
+    ("local-gqa4", spec(16, 4, 128, 512, 512, 64), [700, 129], None),
+    ("global-gqa8", spec(16, 2, 128, 0, 1024, 64), [1300], None),
+    ("local-gqa3", spec(6, 2, 128, 300, 300, 64), [500], None),
+    ("global-gqa3", spec(6, 2, 128, 0, 256, 64), [400], None),
+    # sequence ends just below, at and just above the 64-key tile and the
+    # query tile of either layer kind
+    ("tile-edges-local", spec(4, 2, 128, 512, 512, 64), [63, 64, 65, 127, 128, 129], None),
+    ("tile-edges-global", spec(8, 2, 128, 0, 1024, 64), [63, 64, 65, 127, 128, 129], None),
+    # windows wider and narrower than the bias extent
+    ("local-w300-r64", spec(4, 2, 128, 300, 64, 64), [700], None),
+    ("local-w64-r512", spec(4, 2, 128, 64, 512, 64), [400], None),
 ]
 
 
@@ -165,6 +178,34 @@ def test_zero_bias_is_plain_attention():
     ref = torch.nn.functional.scaled_dot_product_attention(
         q.cpu(), k.cpu(), v.cpu(), is_causal=True, scale=1 / math.sqrt(128))
     assert_parity(out, ref.permute(1, 0, 2).double().numpy(), torch.bfloat16, "zero bias")
+
+
+@pytest.mark.parametrize("W,R,lens", [(96, 128, [300, 70]), (0, 64, [333])])
+def test_zero_keys_bias_only_softmax(W, R, lens):
+    """All keys zero: every score is its bias alone, so each output row is the
+    softmax of the row's visible bias buckets applied to V, computed here
+    directly in float64 (no oracle)."""
+    dev = device()
+    sp = spec(4, 2, 128, W, R, 64)
+    case = ri.make_prefill(sp, lens, seed=23, device=dev, num_pages=None)
+    out = gpu_prefill(case, k_pool=torch.zeros_like(case.k_pool))
+    torch.cuda.synchronize()
+    bias = case.bias.double().cpu()
+    v = case.v_log.double().cpu().repeat_interleave(2, dim=1)      # [T, Hq, D]
+    ref = torch.empty_like(v)
+    cu = case.cu_list()
+    for b, L in enumerate(case.seq_lens):
+        t = torch.arange(L).view(L, 1)
+        s_ = torch.arange(L).view(1, L)
+        d = t - s_
+        vis = (d >= 0) & ((d < W) if W > 0 else torch.ones_like(d, dtype=torch.bool))
+        bucket = d.clamp(0, R - 1)
+        rows = bias[cu[b]:cu[b] + L]                                # [L, Hq, R]
+        logits = torch.gather(rows, 2, bucket.view(L, 1, L).expand(L, 4, L))
+        logits = logits.masked_fill(~vis.view(L, 1, L), float("-inf"))
+        p = torch.softmax(logits, dim=2)
+        ref[cu[b]:cu[b] + L] = torch.einsum("ths,shd->thd", p, v[cu[b]:cu[b] + L])
+    assert_parity(out, ref.numpy(), torch.bfloat16, f"zero keys W={W} R={R}")
 
 
 @pytest.mark.parametrize("name", ["local-prefill-4x4096", "global-prefill-2x16384"])
