@@ -71,11 +71,14 @@ class Oracle:
             fn = getattr(lib, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        hist = lib.rba_oracle_prefill_history
+        hist.argtypes = args[:6] + [ctypes.c_void_p] + args[6:]
+        hist.restype = ctypes.c_int
         self._lib = lib
         self.threads_used = 0
 
     def _run(self, fn, q, k, v, bias, cu, window, rel_extent, sm_scale, rows,
-             want_lse, num_threads):
+             want_lse, num_threads, cu_kv=None):
         q, dt = _as_stored(q)
         k, dk = _as_stored(k)
         v, dv = _as_stored(v)
@@ -96,9 +99,17 @@ class Oracle:
             n_rows = N * Hq
         out = np.zeros((n_rows, D), dtype=np.float64)
         lse = np.zeros((n_rows,), dtype=np.float64) if want_lse else None
-        used = fn(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _arr(cu), len(cu) - 1,
-                  Hq, Hkv, D, R, int(window), float(sm_scale), _arr(rows_arr),
-                  n_rows, _arr(out), _arr(lse), int(num_threads))
+        if cu_kv is None:
+            used = fn(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _arr(cu), len(cu) - 1,
+                      Hq, Hkv, D, R, int(window), float(sm_scale), _arr(rows_arr),
+                      n_rows, _arr(out), _arr(lse), int(num_threads))
+        else:
+            ckv = np.ascontiguousarray(np.asarray(cu_kv, dtype=np.int64))
+            if len(ckv) != len(cu):
+                raise ValueError("cu_q and cu_kv must describe the same sequences")
+            used = fn(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _arr(cu), _arr(ckv),
+                      len(cu) - 1, Hq, Hkv, D, R, int(window), float(sm_scale),
+                      _arr(rows_arr), n_rows, _arr(out), _arr(lse), int(num_threads))
         if used < 0:
             raise ValueError("oracle rejected its arguments")
         self.threads_used = used
@@ -120,6 +131,21 @@ class Oracle:
         """
         return self._run(self._lib.rba_oracle_prefill, q, k, v, bias, cu_seqlens,
                          window, rel_extent, sm_scale, rows, want_lse, num_threads)
+
+    def prefill_history(self, q, k, v, bias, cu_q, cu_kv, *, window: int, rel_extent: int,
+                        sm_scale: float, rows=None, want_lse: bool = False,
+                        num_threads: int = 0):
+        """Reference prefill over a cached history.
+
+        k/v [sum n_b, Hkv, D] hold all n_b logical keys of each sequence back
+        to back (cu_kv [B+1]); q [sum L_b, Hq, D] and bias [sum L_b, Hq, R]
+        hold this call's L_b query tokens (cu_q [B+1]), which are the last
+        L_b positions of their sequence.  ``rows``: optional (query token,
+        head) pairs.
+        """
+        return self._run(self._lib.rba_oracle_prefill_history, q, k, v, bias, cu_q,
+                         window, rel_extent, sm_scale, rows, want_lse, num_threads,
+                         cu_kv=cu_kv)
 
     def decode(self, q, k, v, bias, cu_kv, *, window: int, rel_extent: int,
                sm_scale: float, rows=None, want_lse: bool = False,
@@ -151,3 +177,7 @@ def prefill(*args, **kwargs):
 
 def decode(*args, **kwargs):
     return default().decode(*args, **kwargs)
+
+
+def prefill_history(*args, **kwargs):
+    return default().prefill_history(*args, **kwargs)

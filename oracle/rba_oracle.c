@@ -208,3 +208,60 @@ int rba_oracle_decode(int dtype, const void *q, const void *k, const void *v,
   }
   return bad ? -1 : used;
 }
+
+/*
+ * Prefill over a cached history (chunked prefill; several new tokens of a
+ * decode step).  Sequence b holds n_b keys, rows cu_kv[b] .. cu_kv[b+1]-1 of
+ * the logical K and V tensors [sum n_b, Hkv, D], the keys of this call's
+ * tokens included.  Its L_b = cu_q[b+1] - cu_q[b] query tokens are the last
+ * L_b positions: query token cu_q[b] + i sits at position n_b - L_b + i and
+ * sees the keys the definition above gives for that position.
+ * q [sum L_b, Hq, D], bias [sum L_b, Hq, R] (one row per query token).
+ * rows: optional (query token, head) pairs; NULL means all rows.
+ * Returns -1 on a bad argument, including some L_b > n_b.
+ */
+int rba_oracle_prefill_history(int dtype, const void *q, const void *k,
+                               const void *v, const void *bias,
+                               const int64_t *cu_q, const int64_t *cu_kv,
+                               int num_seqs, int Hq, int Hkv, int D, int R,
+                               int W, double sm_scale, const int64_t *rows,
+                               int64_t n_rows, double *out, double *lse,
+                               int num_threads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || R < 1 || num_seqs < 0) return -1;
+  const int G = Hq / Hkv;
+  const int64_t T = cu_q[num_seqs];
+  int64_t max_keys = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t L = cu_q[b + 1] - cu_q[b], n = cu_kv[b + 1] - cu_kv[b];
+    if (L < 0 || n < L) return -1;
+    if (n > max_keys) max_keys = n;
+  }
+  if (!rows) n_rows = T * Hq;
+  int used = set_threads(num_threads);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *scores = (double *)malloc(sizeof(double) * (size_t)(max_keys + 1));
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      int64_t tok = rows ? rows[2 * r] : r / Hq;
+      int h = rows ? (int)rows[2 * r + 1] : (int)(r % Hq);
+      if (tok < 0 || tok >= T || h < 0 || h >= Hq) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      int b = 0;
+      while (cu_q[b + 1] <= tok) ++b;
+      const int64_t n = cu_kv[b + 1] - cu_kv[b];
+      const int64_t L = cu_q[b + 1] - cu_q[b];
+      const int64_t pos = n - L + (tok - cu_q[b]);
+      attend_row(dtype, q, (tok * Hq + h) * (int64_t)D, k, v,
+                 cu_kv[b] * (int64_t)Hkv * D, Hkv, D, h / G, pos, n, bias,
+                 (tok * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
+                 out + r * (int64_t)D, lse ? lse + r : NULL);
+    }
+    free(scores);
+  }
+  return bad ? -1 : used;
+}

@@ -326,6 +326,86 @@ def pin_decode_is_last_prefill_row(orc):
         assert np.array_equal(dec, pre[last]), (W, R)
 
 
+def _tiny_history(seed, n_keys, n_new, Hq, Hkv, D, R, dtype):
+    """Keys of len n_keys[b] per sequence; queries and bias rows for the last
+    n_new[b] positions."""
+    g = _gen(seed)
+    q = _rand((sum(n_new), Hq, D), g, dtype)
+    k = _rand((sum(n_keys), Hkv, D), g, dtype)
+    v = _rand((sum(n_keys), Hkv, D), g, dtype)
+    b = _rand((sum(n_new), Hq, R), g, dtype)
+    return q, k, v, b
+
+
+def pin_brute_force_prefill_history(orc):
+    """Prefill over a cached history: each new token's row at its absolute
+    position n - L + i against pure-Python brute force."""
+    cases = [
+        # n_keys, n_new, Hq, Hkv, D, W, R, dtype
+        ([9, 20], [3, 20], 4, 2, 4, 0, 6, torch.float32),
+        ([16, 5], [1, 2], 2, 1, 5, 4, 9, torch.bfloat16),
+        ([23], [7], 4, 4, 3, 6, 5, torch.float32),
+    ]
+    for ci, (nk, nq, Hq, Hkv, D, W, R, dt) in enumerate(cases):
+        q, k, v, b = _tiny_history(1300 + ci, nk, nq, Hq, Hkv, D, R, dt)
+        out, lse = orc.prefill_history(q, k, v, b, _cu(nq), _cu(nk), window=W, rel_extent=R,
+                                       sm_scale=0.4, want_lse=True)
+        qd, kd, vd, bd = _f64(q), _f64(k), _f64(v), _f64(b)
+        G = Hq // Hkv
+        cq, ck = _cu(nq), _cu(nk)
+        for bi, (n, L) in enumerate(zip(nk, nq)):
+            for i in range(L):
+                tok = cq[bi] + i
+                for h in range(Hq):
+                    keys = [list(kd[ck[bi] + s, h // G]) for s in range(n)]
+                    vals = [list(vd[ck[bi] + s, h // G]) for s in range(n)]
+                    ref, ref_lse = _brute_row(list(qd[tok, h]), keys, vals, list(bd[tok, h]),
+                                              n - L + i, W, R, 0.4)
+                    assert np.max(np.abs(out[tok, h] - np.array(ref))) < 1e-12, (ci, tok, h)
+                    assert abs(lse[tok, h] - ref_lse) < 1e-12, (ci, tok, h)
+
+
+def pin_history_rows_of_full_prefill(orc):
+    """A prefill of the last L tokens over the first n - L as history returns
+    the last L rows of a plain prefill of all n tokens (chunked prefill
+    changes nothing)."""
+    lens, new = [30, 12, 7], [11, 12, 1]
+    for W, R in ((0, 9), (5, 5), (13, 40)):
+        q, k, v, b = _tiny_prefill(1400 + W, lens, 4, 2, 5, R, torch.bfloat16)
+        full = orc.prefill(q, k, v, b, _cu(lens), window=W, rel_extent=R, sm_scale=0.35)
+        sel = [c - m + i for c, m in zip(_cu(lens)[1:], new) for i in range(m)]
+        part = orc.prefill_history(q[sel], k, v, b[sel], _cu(new), _cu(lens), window=W,
+                                   rel_extent=R, sm_scale=0.35)
+        assert np.array_equal(part, full[sel]), (W, R)
+
+
+def pin_history_single_query_is_decode(orc):
+    """One new token per sequence over its history equals single-token decode."""
+    lens = [6, 17, 1]
+    g = _gen(1500)
+    q = _rand((3, 4, 4), g, torch.float32)
+    k = _rand((sum(lens), 2, 4), g, torch.float32)
+    v = _rand((sum(lens), 2, 4), g, torch.float32)
+    b = _rand((3, 4, 8), g, torch.float32)
+    for W in (0, 4):
+        dec = orc.decode(q, k, v, b, _cu(lens), window=W, rel_extent=8, sm_scale=0.6)
+        hist = orc.prefill_history(q, k, v, b, _cu([1, 1, 1]), _cu(lens), window=W,
+                                   rel_extent=8, sm_scale=0.6)
+        assert np.array_equal(dec, hist), W
+
+
+def pin_history_rejects_more_queries_than_keys(orc):
+    """A sequence with more new tokens than keys is rejected."""
+    q = torch.randn((3, 2, 2))
+    k = torch.randn((2, 1, 2))
+    b = torch.randn((3, 2, 3))
+    try:
+        orc.prefill_history(q, k, k, b, [0, 3], [0, 2], window=0, rel_extent=3, sm_scale=1.0)
+    except ValueError:
+        return
+    raise AssertionError("more queries than keys accepted")
+
+
 def pin_gqa_equals_repeated_mha(orc):
     """GQA equals MHA with every KV head repeated for its query heads."""
     lens = [14, 5]
@@ -411,6 +491,10 @@ ALL_PINS = [
     pin_row_subset_matches,
     pin_worked_example,
     pin_rejects_indivisible_heads,
+    pin_brute_force_prefill_history,
+    pin_history_rows_of_full_prefill,
+    pin_history_single_query_is_decode,
+    pin_history_rejects_more_queries_than_keys,
 ]
 
 

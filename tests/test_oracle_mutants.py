@@ -51,6 +51,12 @@ MUTANTS = [
     ("decode query one past the last key",
      "h / G, n - 1, n, bias,",
      "h / G, n - 2 < 0 ? 0 : n - 2, n, bias,"),
+    ("history ignored: new tokens attend only to each other",
+     "cu_kv[b] * (int64_t)Hkv * D, Hkv, D, h / G, pos, n, bias,",
+     "(cu_kv[b] + n - L) * (int64_t)Hkv * D, Hkv, D, h / G, pos - (n - L), L, bias,"),
+    ("history queries placed at the start of the sequence",
+     "const int64_t pos = n - L + (tok - cu_q[b]);",
+     "const int64_t pos = tok - cu_q[b];"),
     ("no max subtraction lost in normalisation",
      "for (int i = 0; i < D; ++i) out[i] /= l;",
      "for (int i = 0; i < D; ++i) out[i] /= (l + 1e-3);"),
