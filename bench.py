@@ -28,7 +28,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MAIN = "local-prefill-4x4096"
-SECONDARY = ["global-prefill-2x16384", "mixed-decode-256", "long-decode-32x131072"]
+SECONDARY = ["global-prefill-2x16384", "mixed-decode-256", "long-decode-32x131072",
+             "chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384"]
+RIDGE_FLOP_PER_BYTE = 315.0
 
 
 # ---------------------------------------------------------------------------
@@ -57,6 +59,25 @@ def prefill_work(case):
     byt = (T * Hq * D * es * 2                      # q read, out written
            + T * Hkv * D * es * 2                   # k, v
            + Hq * es * sum(bias_entries_prefill(L, W, R) for L in case.seq_lens))
+    return flops, byt
+
+
+def prefill_history_work(case):
+    """Prefill over a cached history: query positions n-L .. n-1 of each
+    sequence; keys visible to any of them are read once."""
+    sp = case.spec
+    D, Hq, Hkv, W, R = sp.head_dim, sp.num_q_heads, sp.num_kv_heads, sp.window, sp.rel_extent
+    es = 2 if str(sp.dtype) == "torch.bfloat16" else 4
+    pairs = bias_entries = kv_keys = 0
+    for n, L in zip(case.key_lens, case.new_lens):
+        for p in range(n - L, n):
+            vis = min(p + 1, W) if W > 0 else p + 1
+            pairs += vis
+            bias_entries += min(vis, R)
+        kv_keys += n - (max(0, n - L - W + 1) if W > 0 else 0)
+    T = case.total_tokens
+    flops = 4 * D * Hq * pairs
+    byt = T * Hq * D * es * 2 + kv_keys * Hkv * D * es * 2 + Hq * es * bias_entries
     return flops, byt
 
 
@@ -201,17 +222,22 @@ def run_decode(cases, splits, steps, warmup, torch, rba):
 def secondary(name, torch, rba, ri, steps, warmup):
     w = ri.WORKLOADS[name]
     cases = ri.build_workload(name, torch.device("cuda:0"))
-    if w["kind"] == "prefill":
+    if w["kind"] in ("prefill", "prefill-history"):
         case = cases["prefill"]
-        flops, byt = prefill_work(case)
+        flops, byt = (prefill_work if w["kind"] == "prefill" else prefill_history_work)(case)
         wall, ev = run_prefill(case, steps, warmup, torch, rba)
         tf = flops / (ev * 1e-3) / 1e12
+        gbs = byt / (ev * 1e-3) / 1e9
+        if w["kind"] == "prefill-history" and flops / byt < RIDGE_FLOP_PER_BYTE:
+            roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        else:
+            roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
         res = {"workload": name, "metric": "prefill attn TFLOP/s", "value": round(tf, 2),
                "unit": "TFLOP/s", "ms_per_step": round(wall, 4), "kernel_ms": round(ev, 4),
-               "roofline": {"bound": "mfma", "achieved": round(tf, 2),
-                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
-               "hbm_gbs": round(byt / (ev * 1e-3) / 1e9, 1)}
+               "roofline": roof, "hbm_gbs": round(gbs, 1),
+               "algorithmic_flops": flops, "algorithmic_bytes": byt}
     else:
         splits = w.get("num_splits", 0)
         flops = byt = 0
@@ -287,6 +313,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v/bias, shuffled page placement)",
     }
+    if w["kind"] == "prefill-history":
+        res = secondary(args.workload, torch, rba, ri, args.steps, args.warmup)
+        result = dict(base, value=res["value"], unit="TFLOP/s", ms_per_step=res["ms_per_step"],
+                      config={"workload": args.workload, "parallelism": "single GPU"},
+                      roofline=dict(res["roofline"], traffic=None, kernel="prefill_bf16_kernel<128>",
+                                    kernel_ms=res["kernel_ms"],
+                                    algorithmic_bytes=res["algorithmic_bytes"],
+                                    algorithmic_flops=res["algorithmic_flops"]))
+        print(json.dumps(result), flush=True)
+        return
     if w["kind"] != "prefill":
         # a decode workload as the main line: throughput in KV-read GB/s
         res = secondary(args.workload, torch, rba, ri, args.steps, args.warmup)

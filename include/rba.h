@@ -72,8 +72,10 @@ typedef enum rba_dtype {
  */
 typedef struct rba_page_table {
   const int32_t *block_table; /* device, [num_seqs][max_pages_per_seq] */
-  const int32_t *seq_lens;    /* device, [num_seqs]: keys held per sequence;
-                                 decode: the current token's key included */
+  const int32_t *seq_lens;    /* device, [num_seqs]: keys held per sequence,
+                                 the keys of this call's tokens included
+                                 (prefill: may be NULL when every sequence
+                                 holds exactly its new tokens) */
   int32_t num_seqs;
   int32_t max_pages_per_seq;
   int32_t page_size;          /* power of two, 16 .. 1024 */
@@ -107,14 +109,23 @@ typedef struct rba_attn_params {
 } rba_attn_params;
 
 /*
- * Prefill: every token of every sequence is a query; the keys of sequence b
- * are its own tokens (positions 0 .. L_b - 1), already written to the pool.
+ * Prefill: every token of this call is a query.  Sequence b holds n_b =
+ * pt->seq_lens[b] keys in the pool, the keys of its L_b new tokens included
+ * (already written); the new tokens are its last L_b positions, so token
+ * cu_seqlens[b]+i sits at position n_b - L_b + i and sees the keys before
+ * it (chunked prefill, or several new tokens of a decode step).  With
+ * n_b == L_b (or seq_lens NULL) this is a plain prefill of whole sequences.
+ * Source of the semantics: the TensorRT-LLM PR #17062 page, Description,
+ * Architecture list (bias per query token, head and distance); the
+ * positions follow from the keys being the sequence's history.
  *
  *  q           [total_tokens][Hq][head_dim]; sequence b owns tokens
- *              cu_seqlens[b] .. cu_seqlens[b+1]-1, token cu_seqlens[b]+t
- *              being position t
+ *              cu_seqlens[b] .. cu_seqlens[b+1]-1
  *  cu_seqlens  device int32 [num_seqs + 1], non-decreasing, cu[0] = 0,
- *              cu[num_seqs] = total_tokens; L_b must equal pt->seq_lens[b]
+ *              cu[num_seqs] = total_tokens
+ *  pt->seq_lens  n_b >= L_b (device data, not checked on the host; a value
+ *              below L_b is read as L_b), n_b <= max_pages_per_seq *
+ *              page_size
  *  max_seqlen  host bound on max_b L_b (sizes the grid)
  *  bias        [total_tokens][Hq][rel_extent]
  *  out         [total_tokens][Hq][head_dim] (written)

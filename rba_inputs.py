@@ -187,6 +187,92 @@ def make_prefill(spec: LayerSpec, seq_lens: List[int], seed: int, device="cpu",
         block_table=table.to(device), k_pool=k_pool, v_pool=v_pool)
 
 
+@dataclasses.dataclass
+class HistoryCase:
+    """Prefill of new tokens over a cached history: sequence b holds
+    key_lens[b] keys in the pool (its new tokens' keys included) and this
+    call's new_lens[b] tokens are its last positions."""
+    spec: LayerSpec
+    new_lens: List[int]
+    key_lens: List[int]
+    q: torch.Tensor               # [sum new, Hq, D]
+    k_log: torch.Tensor           # [sum keys, Hkv, D], sequences back to back
+    v_log: torch.Tensor
+    bias: torch.Tensor            # [sum new, Hq, R]
+    cu_seqlens: torch.Tensor      # int32 [B+1] over the new tokens, device
+    seq_lens_dev: torch.Tensor    # int32 [B] keys per sequence, device
+    block_table: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.new_lens))
+
+    @property
+    def max_seqlen(self) -> int:
+        return int(max(self.new_lens)) if self.new_lens else 0
+
+    def cu_list(self) -> List[int]:
+        return _cumsum(self.new_lens)
+
+    def cu_kv_list(self) -> List[int]:
+        return _cumsum(self.key_lens)
+
+
+def _cumsum(lens):
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    return cu
+
+
+def make_prefill_history(spec: LayerSpec, key_lens: List[int], new_lens: List[int], seed: int,
+                         device="cpu", num_pages: Optional[int] = None,
+                         shuffle: bool = True) -> HistoryCase:
+    """Prefill inputs over a history: all key_lens[b] keys of each sequence
+    are in shuffled pool pages; queries and bias rows exist for the last
+    new_lens[b] positions only."""
+    if any(m > n for m, n in zip(new_lens, key_lens)):
+        raise ValueError("more new tokens than keys")
+    P = spec.page_size
+    B = len(key_lens)
+    g = _dev_gen(seed, device)
+    q = _randn((int(sum(new_lens)), spec.num_q_heads, spec.head_dim), g, device, spec.dtype)
+    k_log = _randn((int(sum(key_lens)), spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    v_log = _randn((int(sum(key_lens)), spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    bias = _randn((int(sum(new_lens)), spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
+                  std=spec.bias_std)
+    pages_per = [max(1, -(-n // P)) for n in key_lens]
+    needed = int(sum(pages_per))
+    if num_pages is None:
+        num_pages = needed
+    if num_pages < needed:
+        raise ValueError("pool too small")
+    cg = _cpu_gen(seed)
+    perm = torch.randperm(num_pages, generator=cg) if shuffle else torch.arange(num_pages)
+    table = torch.zeros((max(B, 1), max(pages_per) if pages_per else 1), dtype=torch.int32)
+    k_pool = torch.full((num_pages, spec.num_kv_heads, P, spec.head_dim), POISON,
+                        dtype=spec.dtype, device=device)
+    v_pool = torch.full_like(k_pool, POISON)
+    off = 0
+    tok = 0
+    for b, n in enumerate(key_lens):
+        pg = perm[off:off + pages_per[b]]
+        table[b, :pages_per[b]] = pg.to(torch.int32)
+        if n > 0:
+            _scatter_pages(k_pool, pg, k_log[tok:tok + n], P)
+            _scatter_pages(v_pool, pg, v_log[tok:tok + n], P)
+        off += pages_per[b]
+        tok += n
+    return HistoryCase(
+        spec=spec, new_lens=list(new_lens), key_lens=list(key_lens), q=q, k_log=k_log,
+        v_log=v_log, bias=bias,
+        cu_seqlens=torch.tensor(_cumsum(new_lens), dtype=torch.int32, device=device),
+        seq_lens_dev=torch.tensor(list(key_lens) or [0], dtype=torch.int32, device=device)[:B],
+        block_table=table.to(device), k_pool=k_pool, v_pool=v_pool)
+
+
 def _seq_kv(spec: LayerSpec, seed: int, b: int, n: int, device):
     g = _dev_gen(seed * 1_000_003 + 7919 * (b + 1), device)
     k = _randn((n, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
@@ -275,6 +361,13 @@ WORKLOADS = {
     "long-decode-32x131072": dict(
         kind="decode", seed=1005, seq_lens=[131072] * 32, num_splits=16,
         spec=LayerSpec(**GLOBAL)),
+    # chunked prefill: the last chunk of each sequence over the cached rest
+    "chunked-local-4x512-ctx4096": dict(
+        kind="prefill-history", seed=1006, key_lens=[4096] * 4, new_lens=[512] * 4,
+        num_pages=512, spec=LayerSpec(**LOCAL)),
+    "chunked-global-2x2048-ctx16384": dict(
+        kind="prefill-history", seed=1007, key_lens=[16384] * 2, new_lens=[2048] * 2,
+        num_pages=512, spec=LayerSpec(**GLOBAL)),
 }
 
 
@@ -292,6 +385,9 @@ def build_workload(name: str, device="cpu"):
                                         num_pages=w["num_pages"], shuffle=w["shuffle"])}
     if w["kind"] == "decode":
         return {"decode": make_decode(w["spec"], w["seq_lens"], w["seed"], device)}
+    if w["kind"] == "prefill-history":
+        return {"prefill": make_prefill_history(w["spec"], w["key_lens"], w["new_lens"], w["seed"],
+                                                device, num_pages=w["num_pages"])}
     if w["kind"] == "mixed-decode":
         lens = mixed_decode_lengths(w["seed"], w["batch"], w["ctx_lo"], w["ctx_hi"])
         return {

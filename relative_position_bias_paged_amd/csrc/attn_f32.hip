@@ -19,8 +19,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int h = blockIdx.y;
   const int tok0 = a.cu_seqlens[b];
   const int L = a.cu_seqlens[b + 1] - tok0;
-  const int t = blockIdx.x * 64 + threadIdx.x;
-  if (t >= L) return;
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= L) return;
+  // this call's L tokens are the last L of the n_k keys held for the
+  // sequence (n_k = L without history): token i sits at position t
+  const int n_k = a.seq_lens != nullptr ? max(a.seq_lens[b], L) : L;
+  const int t = n_k - L + i;
   const int g = h / a.G;
   const int R = a.R, W = a.window, P = a.page_size, lp = a.log2_page;
   const float *qp = static_cast<const float *>(a.q);
@@ -28,7 +32,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const float *vp = static_cast<const float *>(a.v_pool);
   const float *bp = static_cast<const float *>(a.bias);
   const int32_t *trow = a.block_table + (size_t)b * a.max_pages;
-  const size_t row = ((size_t)tok0 + t) * a.Hq + h;
+  const size_t row = ((size_t)tok0 + i) * a.Hq + h;
 
   float q[D];
 #pragma unroll

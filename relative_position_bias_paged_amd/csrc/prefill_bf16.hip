@@ -161,33 +161,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int qb = wave / hpw;
 
   const int tok0 = a.cu_seqlens[b];
-  const int L = a.cu_seqlens[b + 1] - tok0;
+  const int L = a.cu_seqlens[b + 1] - tok0;  // this call's query tokens of the sequence
   const int t0 = qt * QM;
   if (t0 >= L) return;
-  const int tq0 = t0 + 32 * qb;              // this wave's first query
+  // The sequence holds n_k keys, this call's included, and the call's L
+  // tokens are its last L positions: token index i sits at position
+  // hist + i (no key count given: no history).
+  const int n_k = a.seq_lens != nullptr ? max(a.seq_lens[b], L) : L;
+  const int hist = n_k - L;
+  const int tq0 = t0 + 32 * qb;              // this wave's first query (token index)
+  const int pq0 = hist + tq0;                // and its position
 
   const int Hq = a.Hq;
   const int R = a.R;
   const int W = a.window;
-  const int t_last = min(t0 + QM, L) - 1;
-  int s_begin = (W > 0) ? max(0, t0 - W + 1) : 0;
+  const int p_last = hist + min(t0 + QM, L) - 1;   // position of the work-group's last query
+  int s_begin = (W > 0) ? max(0, hist + t0 - W + 1) : 0;
   s_begin &= ~(BN - 1);
 
-  // Key tile s0 (a multiple of BN) against this wave's queries tq0..tq0+31,
-  // each test one compare with a per-wave bound (d = t - s ranges over
-  // [tq0 - s0 - 63, tq0 + 31 - s0]):
+  // Key tile s0 (a multiple of BN) against this wave's queries at positions
+  // pq0..pq0+31, each test one compare with a per-wave bound (d = p - s
+  // ranges over [pq0 - s0 - 63, pq0 + 31 - s0]):
   //   active     s_lo < s0 <= s_hi  some key is visible
   //   band       s0 > s_band        some distance is below R-1 (bias staged)
   //   masked     s0 > s_diag, s0 <= s_wedge or s0 > s_tail
   //              (causal diagonal, window edge, sequence end inside the tile)
   //   beyond     s0 <= s_strad      some distance exceeds R-1
-  const int s_hi = tq0 + 31;
-  const int s_lo = (W > 0) ? tq0 - (BN - 1) - W : INT_MIN;
-  const int s_band = tq0 - (BN - 2) - R;
-  const int s_diag = tq0 - (BN - 1);
-  const int s_wedge = (W > 0) ? tq0 + 31 - W : INT_MIN;
-  const int s_tail = L - BN;
-  const int s_strad = tq0 + 31 - R;
+  const int s_hi = pq0 + 31;
+  const int s_lo = (W > 0) ? pq0 - (BN - 1) - W : INT_MIN;
+  const int s_band = pq0 - (BN - 2) - R;
+  const int s_diag = pq0 - (BN - 1);
+  const int s_wedge = (W > 0) ? pq0 + 31 - W : INT_MIN;
+  const int s_tail = n_k - BN;
+  const int s_strad = pq0 + 31 - R;
   // a layer whose window stays within the R buckets never sees a clamped
   // distance inside its window
   const bool wide_layer = W <= 0 || W > R;
@@ -204,7 +210,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // ---- this lane's query row --------------------------------------------
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int t = tq0 + col;
+  const int t = tq0 + col;                   // token index
+  const int p = hist + t;                    // position
   const bool row_ok = t < L;
   const size_t row = ((size_t)tok0 + (row_ok ? t : 0)) * Hq + h;
 
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const long long v_minus_k = reinterpret_cast<const char *>(vp) - reinterpret_cast<const char *>(kp);
   const uint32_t page_bytes = (uint32_t)(page_stride * 2);   // checked on the host to fit
   auto load_kv = [&](int s0, int page_v, uint16_t *kl, uint16_t *vl) {
-    const int last = L - 1 - s0;        // rows above this repeat the last key
+    const int last = n_k - 1 - s0;      // rows above this repeat the last key
     if constexpr (BIG_PAGE) {
       // the 64-key tile lies inside one page
       const uint32_t page = (uint32_t)__builtin_amdgcn_readfirstlane(page_v);
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int c = (lane & 7) ^ ((rq >> 1) & 7);
     const size_t rrow = ((size_t)tok0 + (tq < L ? tq : 0)) * Hq + h;
     sptr[k] = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.bias) + rrow * R) +
-              2 * (long long)(tq - (BN - 1) + 8 * c);
+              2 * (long long)(hist + tq - (BN - 1) + 8 * c);
   }
   auto stage_bias = [&](int s0) {       // direct loads, tile s0 -> this wave's stage
 #pragma unroll
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       for (int p = 0; p < 4; ++p)
         bp[p] = *reinterpret_cast<const u32x4_t *>(stage_w + col * BN + (((7 - half - 2 * p) ^ sw) * 8));
     } else {
-      const int ds0 = t - s0 - 8 * half - 7;
+      const int ds0 = p - s0 - 8 * half - 7;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         u32x4_t v = zero4;
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
 
     // Element j of 32-key half `sub` is key s0 + 8*half + koff,
     // koff = 32*sub + 16*(j>>3) + (j&7), at distance dq - koff.
-    const int dq = t - s0 - 8 * half;
+    const int dq = p - s0 - 8 * half;
 
     const uint16_t *kt = kl + kbase;
     const uint16_t *vt = vl + vbase;
@@ -400,7 +407,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
           acc[j] = fmaf(acc[j], scale, bf16x8_elem(bp[2 * sub + (j >> 3)], 7 - (j & 7)));
       } else if (path == 2) {
         // visible iff kv_lo < koff <= kv_hi, i.e. (unsigned)(koff - kv_lo - 1) < span
-        const int kv_hi = min(dq, L - 1 - s0 - 8 * half);
+        const int kv_hi = min(dq, n_k - 1 - s0 - 8 * half);
         const int kv_lo1 = (W > 0) ? dq - W + 1 : -(1 << 30);
         const uint32_t span = (uint32_t)max(kv_hi - kv_lo1 + 1, 0);
         if (clamp_free) {
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // the order; on global layers T_first = 0 and the order is the natural one,
   // which already aligns the work-groups.)
   const int T_first = s_begin / BN;
-  const int n_t = t_last / BN - T_first + 1;
+  const int n_t = p_last / BN - T_first + 1;
   const int rot = (n_t - T_first % n_t) % n_t;
   const int s_tfirst = T_first * BN, s_tlast = (T_first + n_t - 1) * BN;
   auto tile_after = [&](int s) { return s == s_tlast ? s_tfirst : s + BN; };

@@ -146,6 +146,7 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
   a.k_pool = kv->k_pool;
   a.v_pool = kv->v_pool;
   a.block_table = pt->block_table;
+  a.seq_lens = pt->seq_lens;       // null: the queries are all the keys
   a.bias = bias;
   a.out = out;
   a.lse = lse;

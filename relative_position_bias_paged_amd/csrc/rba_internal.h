@@ -14,6 +14,7 @@ struct PrefillArgs {
   const void *k_pool;        // [num_pages][Hkv][P][D]
   const void *v_pool;
   const int32_t *block_table; // [B][max_pages]
+  const int32_t *seq_lens;    // prefill: keys held per sequence, this call's included (null: none before it)
   const void *bias;          // [T][Hq][R]
   void *out;                 // [T][Hq][D]
   float *lse;                // [T][Hq] or null

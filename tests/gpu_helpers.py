@@ -67,6 +67,13 @@ def oracle_prefill(case: ri.PrefillCase, rows=None, want_lse=False):
                           rows=rows, want_lse=want_lse)
 
 
+def oracle_prefill_history(case: ri.HistoryCase, rows=None, want_lse=False):
+    sp = case.spec
+    return oracle.prefill_history(case.q, case.k_log, case.v_log, case.bias, case.cu_list(),
+                                  case.cu_kv_list(), window=sp.window, rel_extent=sp.rel_extent,
+                                  sm_scale=sp.scale(), rows=rows, want_lse=want_lse)
+
+
 def gpu_decode(case: ri.DecodeCase, num_splits=0, want_lse=False, block_table=None,
                k_pool=None, v_pool=None, max_seq_len=None):
     sp = case.spec
