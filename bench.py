@@ -29,7 +29,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MAIN = "local-prefill-4x4096"
 SECONDARY = ["global-prefill-2x16384", "mixed-decode-256", "long-decode-32x131072",
-             "chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384"]
+             "chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384", "kv-append-8x2048"]
 RIDGE_FLOP_PER_BYTE = 315.0
 
 
@@ -222,6 +222,22 @@ def run_decode(cases, splits, steps, warmup, torch, rba):
 def secondary(name, torch, rba, ri, steps, warmup):
     w = ri.WORKLOADS[name]
     cases = ri.build_workload(name, torch.device("cuda:0"))
+    if w["kind"] == "append":
+        c = cases["append"]
+        es = 2 if str(c.spec.dtype) == "torch.bfloat16" else 4
+        byt = 2 * 2 * c.k_new.numel() * es          # K and V, each read once and written once
+
+        def step():
+            rba.kv_append(c.k_new, c.v_new, c.cu_new, c.k_pool, c.v_pool, c.block_table,
+                          c.seq_lens_dev)
+
+        wall, ev = time_steps(step, steps, warmup, torch)
+        gbs = byt / (ev * 1e-3) / 1e9
+        return {"workload": name, "metric": "K/V append GB/s", "value": round(gbs, 1),
+                "unit": "GB/s", "ms_per_step": round(wall, 4), "kernel_ms": round(ev, 4),
+                "algorithmic_bytes": byt,
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
     if w["kind"] in ("prefill", "prefill-history"):
         case = cases["prefill"]
         flops, byt = (prefill_work if w["kind"] == "prefill" else prefill_history_work)(case)
@@ -313,6 +329,16 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v/bias, shuffled page placement)",
     }
+    if w["kind"] == "append":
+        res = secondary(args.workload, torch, rba, ri, args.steps, args.warmup)
+        result = dict(base, metric=res["metric"], value=res["value"], unit="GB/s",
+                      ms_per_step=res["ms_per_step"],
+                      config={"workload": args.workload, "parallelism": "single GPU"},
+                      roofline=dict(res["roofline"], traffic=None, kernel="kv_append_kernel",
+                                    kernel_ms=res["kernel_ms"],
+                                    algorithmic_bytes=res["algorithmic_bytes"]))
+        print(json.dumps(result), flush=True)
+        return
     if w["kind"] == "prefill-history":
         res = secondary(args.workload, torch, rba, ri, args.steps, args.warmup)
         result = dict(base, value=res["value"], unit="TFLOP/s", ms_per_step=res["ms_per_step"],

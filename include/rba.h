@@ -193,6 +193,36 @@ rba_status rba_decode(const void *q, const rba_kv_cache *kv,
                       size_t workspace_bytes, void *out, float *lse,
                       hipStream_t stream);
 
+/*
+ * Append: write the keys and values of new tokens into their pool pages, so
+ * that a following rba_prefill or rba_decode reads them.  Sequence b holds
+ * n_b = pt->seq_lens[b] keys after the call, and its L_b new tokens
+ * (cu_new[b] .. cu_new[b+1]-1) are its last L_b positions: new token i goes
+ * to position n_b - L_b + i, pool page
+ * block_table[b * max_pages_per_seq + pos / page_size], slot
+ * pos % page_size (the positional page table of the TensorRT-LLM PR #17860
+ * page, the commit that borrows the framework page table).  Nothing else of
+ * the pools is written.
+ *
+ *  k_new, v_new  [total_new][num_kv_heads][head_dim], the pool dtype,
+ *                16-byte aligned
+ *  cu_new        device int32 [num_seqs + 1], non-decreasing, cu[0] = 0,
+ *                cu[num_seqs] = total_new
+ *  pt->seq_lens  device, required; n_b >= L_b.  A position past
+ *                max_pages_per_seq * page_size, or a table entry outside
+ *                [0, num_pages), leaves that token's rows unwritten.
+ *
+ * The call reads no device data on the host and allocates nothing, so it
+ * can be captured in a HIP graph together with the decode that follows.
+ * RBA_ERR_INVALID_ARG for a null or misaligned pointer, a negative count,
+ * a page_size that is not a power of two; RBA_ERR_UNSUPPORTED for a
+ * head_dim or page_size outside the ranges of rba_prefill.  total_new == 0
+ * or num_seqs == 0 is a no-op returning RBA_OK.
+ */
+rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu_new,
+                         int32_t total_new, const rba_kv_cache *kv,
+                         const rba_page_table *pt, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char *rba_status_string(rba_status status);
 

@@ -273,6 +273,46 @@ def make_prefill_history(spec: LayerSpec, key_lens: List[int], new_lens: List[in
         block_table=table.to(device), k_pool=k_pool, v_pool=v_pool)
 
 
+@dataclasses.dataclass
+class AppendCase:
+    """New tokens' keys and values to write into shuffled pool pages; the
+    sequences hold key_lens[b] keys after the append."""
+    spec: LayerSpec
+    new_lens: List[int]
+    key_lens: List[int]
+    k_new: torch.Tensor           # [sum new, Hkv, D]
+    v_new: torch.Tensor
+    cu_new: torch.Tensor          # int32 [B+1], device
+    seq_lens_dev: torch.Tensor    # int32 [B] keys after the append, device
+    block_table: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+
+
+def make_append(spec: LayerSpec, key_lens: List[int], new_lens: List[int], seed: int,
+                device="cpu") -> AppendCase:
+    P = spec.page_size
+    g = _dev_gen(seed, device)
+    T = int(sum(new_lens))
+    k_new = _randn((T, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    v_new = _randn((T, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
+    pages_per = [max(1, -(-n // P)) for n in key_lens]
+    num_pages = int(sum(pages_per))
+    perm = torch.randperm(num_pages, generator=_cpu_gen(seed))
+    table = torch.zeros((len(key_lens), max(pages_per)), dtype=torch.int32)
+    off = 0
+    for b, npg in enumerate(pages_per):
+        table[b, :npg] = perm[off:off + npg].to(torch.int32)
+        off += npg
+    k_pool = torch.zeros((num_pages, spec.num_kv_heads, P, spec.head_dim), dtype=spec.dtype,
+                         device=device)
+    return AppendCase(spec=spec, new_lens=list(new_lens), key_lens=list(key_lens), k_new=k_new,
+                      v_new=v_new,
+                      cu_new=torch.tensor(_cumsum(new_lens), dtype=torch.int32, device=device),
+                      seq_lens_dev=torch.tensor(key_lens, dtype=torch.int32, device=device),
+                      block_table=table.to(device), k_pool=k_pool, v_pool=torch.zeros_like(k_pool))
+
+
 def _seq_kv(spec: LayerSpec, seed: int, b: int, n: int, device):
     g = _dev_gen(seed * 1_000_003 + 7919 * (b + 1), device)
     k = _randn((n, spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
@@ -361,6 +401,11 @@ WORKLOADS = {
     "long-decode-32x131072": dict(
         kind="decode", seed=1005, seq_lens=[131072] * 32, num_splits=16,
         spec=LayerSpec(**GLOBAL)),
+    # K/V append of a prefill chunk: 8 sequences, 2048 new tokens each onto
+    # 2048 cached ones, local-layer pools
+    "kv-append-8x2048": dict(
+        kind="append", seed=1008, key_lens=[4096] * 8, new_lens=[2048] * 8,
+        spec=LayerSpec(**LOCAL)),
     # chunked prefill: the last chunk of each sequence over the cached rest
     "chunked-local-4x512-ctx4096": dict(
         kind="prefill-history", seed=1006, key_lens=[4096] * 4, new_lens=[512] * 4,
@@ -385,6 +430,8 @@ def build_workload(name: str, device="cpu"):
                                         num_pages=w["num_pages"], shuffle=w["shuffle"])}
     if w["kind"] == "decode":
         return {"decode": make_decode(w["spec"], w["seq_lens"], w["seed"], device)}
+    if w["kind"] == "append":
+        return {"append": make_append(w["spec"], w["key_lens"], w["new_lens"], w["seed"], device)}
     if w["kind"] == "prefill-history":
         return {"prefill": make_prefill_history(w["spec"], w["key_lens"], w["new_lens"], w["seed"],
                                                 device, num_pages=w["num_pages"])}

@@ -33,7 +33,7 @@ RBA_F32 = 1
 
 # every symbol include/rba.h declares
 EXPORTED = ("rba_prefill", "rba_decode", "rba_decode_num_splits",
-            "rba_decode_workspace_size", "rba_status_string")
+            "rba_decode_workspace_size", "rba_kv_append", "rba_status_string")
 
 
 class rba_page_table(ctypes.Structure):
@@ -100,6 +100,9 @@ def load():
     lib.rba_decode_workspace_size.argtypes = [P(rba_kv_cache), P(rba_page_table), ctypes.c_int32,
                                               P(rba_attn_params), ctypes.c_int32]
     lib.rba_decode_workspace_size.restype = ctypes.c_size_t
+    lib.rba_kv_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                  P(rba_kv_cache), P(rba_page_table), ctypes.c_void_p]
+    lib.rba_kv_append.restype = ctypes.c_int
     lib.rba_status_string.argtypes = [ctypes.c_int]
     lib.rba_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -192,6 +195,29 @@ def prefill(q: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
                          _stream(stream))
     _check(st, "rba_prefill")
     return out
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_new: torch.Tensor,
+              k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+              seq_lens: torch.Tensor, *, stream=None) -> None:
+    """rba_kv_append: k_new/v_new [total_new,Hkv,D] into the pools; seq_lens
+    are the key counts after the append (the new tokens are the last ones)."""
+    lib = load()
+    if k_new.dim() != 3 or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must both be [total_new, Hkv, head_dim]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("new keys/values and the pools must share one dtype")
+    if k_new.shape[1:] != (k_pool.shape[1], k_pool.shape[3]):
+        raise ValueError("k_new heads/head_dim differ from the pool")
+    if cu_new.numel() != block_table.shape[0] + 1:
+        raise ValueError("cu_new must have num_seqs + 1 entries")
+    if seq_lens is None:
+        raise ValueError("seq_lens is required")
+    kv, pt, _ = _structs(k_pool, v_pool, block_table, seq_lens, k_pool.shape[1], 0, 1, 1.0)
+    st = lib.rba_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                           _dev(cu_new, "cu_new", torch.int32), int(k_new.shape[0]),
+                           ctypes.byref(kv), ctypes.byref(pt), _stream(stream))
+    _check(st, "rba_kv_append")
 
 
 def _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale):

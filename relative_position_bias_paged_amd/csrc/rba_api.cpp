@@ -186,6 +186,40 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
   return err == hipSuccess ? RBA_OK : RBA_ERR_HIP;
 }
 
+RBA_EXPORT rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu_new,
+                                    int32_t total_new, const rba_kv_cache *kv,
+                                    const rba_page_table *pt, hipStream_t stream) {
+  if (kv == nullptr || pt == nullptr) return RBA_ERR_INVALID_ARG;
+  if (kv->dtype != RBA_BF16 && kv->dtype != RBA_F32) return RBA_ERR_INVALID_ARG;
+  if (kv->num_kv_heads <= 0 || kv->head_dim <= 0) return RBA_ERR_INVALID_ARG;
+  if (!is_pow2(pt->page_size)) return RBA_ERR_INVALID_ARG;
+  if (total_new < 0 || pt->num_seqs < 0 || pt->max_pages_per_seq < 0 || pt->num_pages < 0)
+    return RBA_ERR_INVALID_ARG;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return RBA_ERR_UNSUPPORTED;
+  if (pt->page_size < 16 || pt->page_size > 1024) return RBA_ERR_UNSUPPORTED;
+  if (total_new == 0 || pt->num_seqs == 0) return RBA_OK;
+  if (k_new == nullptr || v_new == nullptr || cu_new == nullptr || pt->seq_lens == nullptr ||
+      !aligned16(k_new) || !aligned16(v_new) || !pool_ok(kv, pt))
+    return RBA_ERR_INVALID_ARG;
+  rba::AppendArgs a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cu_new = cu_new;
+  a.seq_lens = pt->seq_lens;
+  a.block_table = pt->block_table;
+  a.k_pool = const_cast<void *>(kv->k_pool);
+  a.v_pool = const_cast<void *>(kv->v_pool);
+  a.total_new = total_new;
+  a.num_seqs = pt->num_seqs;
+  a.Hkv = kv->num_kv_heads;
+  a.max_pages = pt->max_pages_per_seq;
+  a.page_size = pt->page_size;
+  a.log2_page = ilog2(pt->page_size);
+  a.num_pages = pt->num_pages;
+  a.row_bytes = kv->head_dim * (kv->dtype == RBA_BF16 ? 2 : 4);
+  return rba::launch_kv_append(a, stream) == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}
+
 RBA_EXPORT int32_t rba_decode_num_splits(const rba_kv_cache *kv, const rba_page_table *pt,
                                          int32_t max_seq_len, const rba_attn_params *params,
                                          int32_t num_splits) {

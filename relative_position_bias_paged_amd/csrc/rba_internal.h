@@ -48,7 +48,21 @@ struct DecodeArgs {
   float sm_scale;
 };
 
+// Arguments of the K/V append kernel.
+struct AppendArgs {
+  const void *k_new;          // [total_new][Hkv][D]
+  const void *v_new;
+  const int32_t *cu_new;      // [B+1] over the new tokens
+  const int32_t *seq_lens;    // [B] keys held after the append
+  const int32_t *block_table; // [B][max_pages]
+  void *k_pool;               // [num_pages][Hkv][P][D]
+  void *v_pool;
+  int32_t total_new, num_seqs, Hkv, max_pages, page_size, log2_page, num_pages;
+  int32_t row_bytes;          // head_dim * element size, a multiple of 16
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);

@@ -164,6 +164,40 @@ def test_decode_split_plan():
     assert plan(1000, 0, hq=31) == (0, 0)
 
 
+def _append(kv, pt, k=FAKE, v=FAKE, cu=FAKE, total=10):
+    return rba.load().rba_kv_append(k, v, cu, total, ctypes.byref(kv), ctypes.byref(pt), None)
+
+
+@pytest.mark.parametrize("kwargs,expected", [
+    (dict(k=None), rba.RBA_ERR_INVALID_ARG),
+    (dict(v=None), rba.RBA_ERR_INVALID_ARG),
+    (dict(cu=None), rba.RBA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 4), rba.RBA_ERR_INVALID_ARG),
+    (dict(total=-1), rba.RBA_ERR_INVALID_ARG),
+])
+def test_append_argument_errors(kwargs, expected):
+    kv, pt, _ = _layer()
+    assert _append(kv, pt, **kwargs) == expected
+
+
+def test_append_layer_errors():
+    kv, pt, _ = _layer(lens=None)
+    assert _append(kv, pt) == rba.RBA_ERR_INVALID_ARG          # seq_lens is required
+    kv, pt, _ = _layer(page=48)
+    assert _append(kv, pt) == rba.RBA_ERR_INVALID_ARG          # page size not a power of two
+    kv, pt, _ = _layer(d=96)
+    assert _append(kv, pt) == rba.RBA_ERR_UNSUPPORTED
+    kv, pt, _ = _layer(page=2048)
+    assert _append(kv, pt) == rba.RBA_ERR_UNSUPPORTED
+
+
+def test_append_empty_is_noop():
+    kv, pt, _ = _layer()
+    assert _append(kv, pt, k=None, v=None, cu=None, total=0) == rba.RBA_OK
+    kv, pt, _ = _layer(seqs=0)
+    assert _append(kv, pt, k=None, total=5) == rba.RBA_OK
+
+
 def test_status_strings():
     for code, name in [(0, "RBA_OK"), (1, "RBA_ERR_INVALID_ARG"), (2, "RBA_ERR_UNSUPPORTED"),
                        (3, "RBA_ERR_WORKSPACE"), (4, "RBA_ERR_HIP")]:
