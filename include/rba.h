@@ -223,6 +223,21 @@ rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu
                          int32_t total_new, const rba_kv_cache *kv,
                          const rba_page_table *pt, hipStream_t stream);
 
+/*
+ * Pages per sequence of a window-only pool for a layer with the given
+ * window: a call that appends or queries at most max_new positions of a
+ * sequence reads keys from at most window + max_new - 1 consecutive
+ * positions, which span at most ceil((window + max_new - 1) / page_size) + 1
+ * pages.  A pool that gives each sequence a ring of that many pages, with
+ * block_table entry j = ring[j % ring_pages] (entries stay positional),
+ * holds every key the kernels read for that layer: its memory is
+ * O(window + max_new) per sequence instead of O(sequence length) (the
+ * window-sized cache the vLLM PR #48768 page notes for its MLX port).
+ * Returns 0 for window <= 0 (a full-causal layer needs every page), a page
+ * size that is not a power of two, or max_new < 1.  Host only.
+ */
+int32_t rba_window_ring_pages(int32_t window, int32_t page_size, int32_t max_new);
+
 /* Static, human-readable name of a status code. */
 const char *rba_status_string(rba_status status);
 

@@ -33,7 +33,8 @@ RBA_F32 = 1
 
 # every symbol include/rba.h declares
 EXPORTED = ("rba_prefill", "rba_decode", "rba_decode_num_splits",
-            "rba_decode_workspace_size", "rba_kv_append", "rba_status_string")
+            "rba_decode_workspace_size", "rba_kv_append", "rba_window_ring_pages",
+            "rba_status_string")
 
 
 class rba_page_table(ctypes.Structure):
@@ -103,6 +104,8 @@ def load():
     lib.rba_kv_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                   P(rba_kv_cache), P(rba_page_table), ctypes.c_void_p]
     lib.rba_kv_append.restype = ctypes.c_int
+    lib.rba_window_ring_pages.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.rba_window_ring_pages.restype = ctypes.c_int32
     lib.rba_status_string.argtypes = [ctypes.c_int]
     lib.rba_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -218,6 +221,22 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_new: torch.Tensor,
                            _dev(cu_new, "cu_new", torch.int32), int(k_new.shape[0]),
                            ctypes.byref(kv), ctypes.byref(pt), _stream(stream))
     _check(st, "rba_kv_append")
+
+
+def window_ring_pages(window: int, page_size: int, max_new: int = 1) -> int:
+    """rba_window_ring_pages: pages per sequence of a window-only pool."""
+    return int(load().rba_window_ring_pages(int(window), int(page_size), int(max_new)))
+
+
+def ring_block_table(rings: torch.Tensor, max_pages_per_seq: int) -> torch.Tensor:
+    """Positional block table over per-sequence page rings: entry j of
+    sequence b is rings[b][j % ring_pages].  rings: int32 [num_seqs,
+    ring_pages] (any device); returns int32 [num_seqs, max_pages_per_seq] on
+    the same device.  Host-side index arithmetic only."""
+    if rings.dim() != 2 or rings.dtype != torch.int32:
+        raise ValueError("rings must be int32 [num_seqs, ring_pages]")
+    j = torch.arange(max_pages_per_seq, device=rings.device) % rings.shape[1]
+    return rings[:, j].contiguous()
 
 
 def _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale):

@@ -220,6 +220,13 @@ RBA_EXPORT rba_status rba_kv_append(const void *k_new, const void *v_new, const 
   return rba::launch_kv_append(a, stream) == hipSuccess ? RBA_OK : RBA_ERR_HIP;
 }
 
+RBA_EXPORT int32_t rba_window_ring_pages(int32_t window, int32_t page_size, int32_t max_new) {
+  if (window <= 0 || max_new < 1 || !is_pow2(page_size)) return 0;
+  const long long span = (long long)window + max_new - 1;      // consecutive key positions read
+  const long long pages = (span + page_size - 1) / page_size + 1;
+  return pages > 0x7fffffffLL ? 0 : (int32_t)pages;
+}
+
 RBA_EXPORT int32_t rba_decode_num_splits(const rba_kv_cache *kv, const rba_page_table *pt,
                                          int32_t max_seq_len, const rba_attn_params *params,
                                          int32_t num_splits) {

@@ -198,6 +198,30 @@ def test_append_empty_is_noop():
     assert _append(kv, pt, k=None, total=5) == rba.RBA_OK
 
 
+def test_window_ring_pages():
+    # window 512, 64-token pages, one new token: 512 positions span 9 pages
+    assert rba.window_ring_pages(512, 64, 1) == 9
+    # a 512-token chunk over a 512 window: 1023 positions, up to 17 pages
+    assert rba.window_ring_pages(512, 64, 512) == 17
+    assert rba.window_ring_pages(100, 16, 1) == 8
+    assert rba.window_ring_pages(0, 64, 1) == 0          # full causal: no ring
+    assert rba.window_ring_pages(512, 48, 1) == 0        # not a power of two
+    assert rba.window_ring_pages(512, 64, 0) == 0
+    # brute force: every start position of a span lies in at most that many pages
+    for W, P, m in ((512, 64, 1), (100, 16, 7), (64, 64, 64), (33, 32, 1)):
+        span = W + m - 1
+        worst = max((s + span - 1) // P - s // P + 1 for s in range(4 * P))
+        assert rba.window_ring_pages(W, P, m) >= worst
+        assert rba.window_ring_pages(W, P, m) <= worst + 1
+
+
+def test_ring_block_table_is_positional():
+    import torch
+    rings = torch.tensor([[7, 3, 9], [0, 1, 2]], dtype=torch.int32)
+    t = rba.ring_block_table(rings, 8)
+    assert t.tolist() == [[7, 3, 9, 7, 3, 9, 7, 3], [0, 1, 2, 0, 1, 2, 0, 1]]
+
+
 def test_status_strings():
     for code, name in [(0, "RBA_OK"), (1, "RBA_ERR_INVALID_ARG"), (2, "RBA_ERR_UNSUPPORTED"),
                        (3, "RBA_ERR_WORKSPACE"), (4, "RBA_ERR_HIP")]:
