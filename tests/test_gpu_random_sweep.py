@@ -1,0 +1,102 @@
+"""Seeded random sweep of shapes through every GPU entry point against the
+oracle: query/KV head counts with GQA 1..8, head_dim 64/128, windows shorter
+and longer than the bias extent (and full causal), extents from 1 to beyond
+the sequence, page sizes 16..256, ragged and empty sequences, histories, and
+forced decode partition counts.  Sizes stay small enough for the oracle to
+check every row.
+"""
+import random
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import rba_inputs as ri
+from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, gpu_decode, gpu_prefill,
+                         oracle_decode, oracle_prefill, oracle_prefill_history)
+
+pytestmark = pytest.mark.gpu
+
+
+def _random_spec(rng, dtype=torch.bfloat16):
+    hkv = rng.choice([1, 2, 3, 4])
+    G = rng.choice([1, 2, 3, 4, 8])
+    W = rng.choice([0, 0, 1, 17, 64, 100, 256, 512])
+    R = rng.choice([1, 7, 64, 100, 256, 512, 1024])
+    return ri.LayerSpec(num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=rng.choice([64, 128]),
+                        window=W, rel_extent=R, page_size=rng.choice([16, 32, 64, 128, 256]),
+                        dtype=dtype)
+
+
+def _cases(kind, n):
+    rng = random.Random(zlib.crc32(kind.encode()))
+    return [(i, rng.randrange(1 << 30)) for i in range(n)]
+
+
+@pytest.mark.parametrize("i,seed", _cases("prefill", 16))
+def test_random_prefill(i, seed):
+    rng = random.Random(seed)
+    sp = _random_spec(rng)
+    lens = [rng.choice([0, 1, 2, 31, 63, 64, 65, 127, 129, 200, 333, 700])
+            for _ in range(rng.randint(1, 4))]
+    if sum(lens) == 0:
+        lens[0] = 5
+    case = ri.make_prefill(sp, lens, seed=seed % 100000, device=device())
+    out, lse = gpu_prefill(case, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_prefill(case, want_lse=True)
+    what = f"prefill #{i} {sp} lens={lens}"
+    assert_parity(out, ref, sp.dtype, what)
+    assert np.max(np.abs(lse.cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS, what
+
+
+@pytest.mark.parametrize("i,seed", _cases("history", 12))
+def test_random_prefill_history(i, seed):
+    rng = random.Random(seed)
+    sp = _random_spec(rng)
+    B = rng.randint(1, 4)
+    keys = [rng.choice([1, 5, 64, 65, 130, 400, 1000]) for _ in range(B)]
+    new = [rng.randint(1, k) if rng.random() < 0.7 else k for k in keys]
+    case = ri.make_prefill_history(sp, keys, new, seed=seed % 100000, device=device())
+    out, lse = gpu_prefill(case, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_prefill_history(case, want_lse=True)
+    what = f"history #{i} {sp} keys={keys} new={new}"
+    assert_parity(out, ref, sp.dtype, what)
+    assert np.max(np.abs(lse.cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS, what
+
+
+@pytest.mark.parametrize("i,seed", _cases("decode", 16))
+def test_random_decode(i, seed):
+    rng = random.Random(seed)
+    sp = _random_spec(rng)
+    lens = [rng.choice([0, 1, 2, 63, 64, 65, 300, 1000, 2500, 5000])
+            for _ in range(rng.randint(1, 6))]
+    window_only = sp.window > 0 and rng.random() < 0.5
+    case = ri.make_decode(sp, lens, seed=seed % 100000, device=device(), window_only=window_only)
+    splits = rng.choice([0, 0, 1, 3, 16, 64])
+    out, lse = gpu_decode(case, num_splits=splits, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode(case, want_lse=True)
+    what = f"decode #{i} {sp} lens={lens} splits={splits} window_only={window_only}"
+    assert_parity(out, ref, sp.dtype, what)
+    g = lse.cpu().double().numpy()
+    both_empty = np.isneginf(g) & np.isneginf(ref_lse)     # empty sequences: -inf on both sides
+    diff = np.zeros_like(g)
+    np.subtract(g, ref_lse, out=diff, where=~both_empty)
+    assert np.max(np.abs(diff)) <= LSE_MAX_ABS, what
+
+
+@pytest.mark.parametrize("i,seed", _cases("fp32", 6))
+def test_random_fp32(i, seed):
+    rng = random.Random(seed)
+    sp = _random_spec(rng, dtype=torch.float32)
+    lens = [rng.choice([1, 17, 64, 100, 200]) for _ in range(rng.randint(1, 3))]
+    pre = ri.make_prefill(sp, lens, seed=seed % 100000, device=device())
+    out = gpu_prefill(pre)
+    dec = ri.make_decode(sp, lens, seed=seed % 100000 + 1, device=device())
+    dout = gpu_decode(dec, num_splits=rng.choice([0, 1, 4]))
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_prefill(pre), torch.float32, f"fp32 prefill #{i} {sp}")
+    assert_parity(dout, oracle_decode(dec), torch.float32, f"fp32 decode #{i} {sp}")
