@@ -74,6 +74,12 @@ class Oracle:
         hist = lib.rba_oracle_prefill_history
         hist.argtypes = args[:6] + [ctypes.c_void_p] + args[6:]
         hist.restype = ctypes.c_int
+        proj = lib.rba_oracle_prefill_projected
+        proj.argtypes = ([ctypes.c_int] + [ctypes.c_void_p] * 7
+                         + [ctypes.c_int] * 6 + [ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
+                                                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_int])
+        proj.restype = ctypes.c_int
         self._lib = lib
         self.threads_used = 0
 
@@ -147,6 +153,53 @@ class Oracle:
                          window, rel_extent, sm_scale, rows, want_lse, num_threads,
                          cu_kv=cu_kv)
 
+    def prefill_projected(self, q, k, v, rel_r, w_rel, cu_q, cu_kv=None, *, window: int,
+                          sm_scale: float, rows=None, want_lse: bool = False,
+                          num_threads: int = 0):
+        """Prefill whose bias is the projection bias[t,h,d] = sum_k rel_r[t,h,k] w_rel[k,d].
+
+        rel_r [sum L_b, Hq, d_rel], w_rel [d_rel, R] (the pages' layout); the
+        rest as ``prefill`` (cu_kv None) or ``prefill_history`` (cu_kv given).
+        """
+        q, dt = _as_stored(q)
+        k, dk = _as_stored(k)
+        v, dv = _as_stored(v)
+        rel_r, dr = _as_stored(rel_r)
+        w_rel, dw = _as_stored(w_rel)
+        if len({dt, dk, dv, dr, dw}) != 1:
+            raise TypeError("q, k, v, rel_r and w_rel must share one dtype")
+        N, Hq, D = q.shape
+        Hkv = k.shape[1]
+        d_rel, R = w_rel.shape
+        if rel_r.shape != (N, Hq, d_rel):
+            raise ValueError("rel_r must be [T, Hq, d_rel] with the d_rel of w_rel")
+        cu = np.ascontiguousarray(np.asarray(cu_q, dtype=np.int64))
+        ckv = None
+        if cu_kv is not None:
+            ckv = np.ascontiguousarray(np.asarray(cu_kv, dtype=np.int64))
+            if len(ckv) != len(cu):
+                raise ValueError("cu_q and cu_kv must describe the same sequences")
+        rows_arr = None
+        if rows is not None:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+            n_rows = rows_arr.shape[0]
+        else:
+            n_rows = N * Hq
+        out = np.zeros((n_rows, D), dtype=np.float64)
+        lse = np.zeros((n_rows,), dtype=np.float64) if want_lse else None
+        used = self._lib.rba_oracle_prefill_projected(
+            dt, _ptr(q), _ptr(k), _ptr(v), _ptr(rel_r), _ptr(w_rel), _arr(cu), _arr(ckv),
+            len(cu) - 1, Hq, Hkv, D, R, int(window), d_rel, float(sm_scale), _arr(rows_arr),
+            n_rows, _arr(out), _arr(lse), int(num_threads))
+        if used < 0:
+            raise ValueError("oracle rejected its arguments")
+        self.threads_used = used
+        if rows is None:
+            out = out.reshape(N, Hq, D)
+            if lse is not None:
+                lse = lse.reshape(N, Hq)
+        return (out, lse) if want_lse else out
+
     def decode(self, q, k, v, bias, cu_kv, *, window: int, rel_extent: int,
                sm_scale: float, rows=None, want_lse: bool = False,
                num_threads: int = 0):
@@ -181,3 +234,7 @@ def decode(*args, **kwargs):
 
 def prefill_history(*args, **kwargs):
     return default().prefill_history(*args, **kwargs)
+
+
+def prefill_projected(*args, **kwargs):
+    return default().prefill_projected(*args, **kwargs)

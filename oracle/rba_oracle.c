@@ -51,9 +51,11 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_F64 2 /* bias rows formed here (rba_oracle_prefill_projected) */
 
 /* Widen element i of a tensor stored as fp32 or bf16 to double (exact). */
 static double elem(const void *base, int dtype, int64_t i) {
+  if (dtype == ORC_F64) return ((const double *)base)[i];
   if (dtype == ORC_F32) return (double)((const float *)base)[i];
   uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
   float f;
@@ -71,8 +73,9 @@ static double elem(const void *base, int dtype, int64_t i) {
 static void attend_row(int dtype, const void *q, int64_t q_row, const void *k,
                        const void *v, int64_t kv0, int Hkv, int D, int g,
                        int64_t t, int64_t n_keys, const void *bias,
-                       int64_t bias_row, int R, int W, double sm_scale,
-                       double *scores, double *out, double *lse) {
+                       int bias_dtype, int64_t bias_row, int R, int W,
+                       double sm_scale, double *scores, double *out,
+                       double *lse) {
   const int64_t kv_stride = (int64_t)Hkv * D;
   double m = -INFINITY;
   for (int64_t s = 0; s < n_keys; ++s) {
@@ -87,7 +90,7 @@ static void attend_row(int dtype, const void *q, int64_t q_row, const void *k,
              elem(k, dtype, kv0 + s * kv_stride + (int64_t)g * D + i);
     int64_t d = t - s;
     if (d > R - 1) d = R - 1;
-    scores[s] = sm_scale * dot + elem(bias, dtype, bias_row + d);
+    scores[s] = sm_scale * dot + elem(bias, bias_dtype, bias_row + d);
     if (scores[s] > m) m = scores[s];
   }
   for (int i = 0; i < D; ++i) out[i] = 0.0;
@@ -158,7 +161,7 @@ int rba_oracle_prefill(int dtype, const void *q, const void *k, const void *v,
       int64_t len = cu_seqlens[b + 1] - start;
       attend_row(dtype, q, (tok * Hq + h) * (int64_t)D, k, v,
                  start * (int64_t)Hkv * D, Hkv, D, h / G, tok - start, len,
-                 bias, (tok * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
+                 bias, dtype, (tok * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
                  out + r * (int64_t)D, lse ? lse + r : NULL);
     }
     free(scores);
@@ -201,7 +204,7 @@ int rba_oracle_decode(int dtype, const void *q, const void *k, const void *v,
       int64_t n = cu_kv[b + 1] - cu_kv[b];
       attend_row(dtype, q, (b * Hq + h) * (int64_t)D, k, v,
                  cu_kv[b] * (int64_t)Hkv * D, Hkv, D, h / G, n - 1, n, bias,
-                 (b * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
+                 dtype, (b * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
                  out + r * (int64_t)D, lse ? lse + r : NULL);
     }
     free(scores);
@@ -258,9 +261,81 @@ int rba_oracle_prefill_history(int dtype, const void *q, const void *k,
       const int64_t pos = n - L + (tok - cu_q[b]);
       attend_row(dtype, q, (tok * Hq + h) * (int64_t)D, k, v,
                  cu_kv[b] * (int64_t)Hkv * D, Hkv, D, h / G, pos, n, bias,
-                 (tok * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
+                 dtype, (tok * Hq + h) * (int64_t)R, R, W, sm_scale, scores,
                  out + r * (int64_t)D, lse ? lse + r : NULL);
     }
+    free(scores);
+  }
+  return bad ? -1 : used;
+}
+
+/*
+ * Prefill with the bias given by its projection instead of a tensor:
+ *
+ *   bias[t,h,d] = sum_k r[t,h,k] * w[k,d],   d = 0 .. R-1,
+ *
+ * r [sum L_b, Hq, d_rel] one row per query token, w [d_rel, R]: the product
+ * the TensorRT-LLM PR #17062 page's review comment on _build_rel_logits forms
+ * (r of shape [T, heads, d_rel] times rel_logits_proj [d_rel, rel_extent],
+ * giving the [T, heads, rel_extent] bias).  Each needed bias row is formed
+ * here in fp64 from the stored r and w, then the row is attended exactly as
+ * rba_oracle_prefill_history does with its bias tensor.  cu_kv NULL: no
+ * history, every sequence's keys are its query tokens (rba_oracle_prefill).
+ * rows, out, lse and the return value as there.
+ */
+int rba_oracle_prefill_projected(int dtype, const void *q, const void *k,
+                                 const void *v, const void *r, const void *w,
+                                 const int64_t *cu_q, const int64_t *cu_kv,
+                                 int num_seqs, int Hq, int Hkv, int D, int R,
+                                 int W, int d_rel, double sm_scale,
+                                 const int64_t *rows, int64_t n_rows,
+                                 double *out, double *lse, int num_threads) {
+  if (Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || R < 1 || d_rel < 1 || num_seqs < 0)
+    return -1;
+  const int G = Hq / Hkv;
+  const int64_t T = cu_q[num_seqs];
+  int64_t max_keys = 0;
+  for (int b = 0; b < num_seqs; ++b) {
+    const int64_t L = cu_q[b + 1] - cu_q[b];
+    const int64_t n = cu_kv ? cu_kv[b + 1] - cu_kv[b] : L;
+    if (L < 0 || n < L) return -1;
+    if (n > max_keys) max_keys = n;
+  }
+  if (!rows) n_rows = T * Hq;
+  int used = set_threads(num_threads);
+  int bad = 0;
+#pragma omp parallel
+  {
+    double *scores = (double *)malloc(sizeof(double) * (size_t)(max_keys + 1));
+    double *brow = (double *)malloc(sizeof(double) * (size_t)R);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t i = 0; i < n_rows; ++i) {
+      int64_t tok = rows ? rows[2 * i] : i / Hq;
+      int h = rows ? (int)rows[2 * i + 1] : (int)(i % Hq);
+      if (tok < 0 || tok >= T || h < 0 || h >= Hq) {
+#pragma omp atomic write
+        bad = 1;
+        continue;
+      }
+      int b = 0;
+      while (cu_q[b + 1] <= tok) ++b;
+      const int64_t L = cu_q[b + 1] - cu_q[b];
+      const int64_t n = cu_kv ? cu_kv[b + 1] - cu_kv[b] : L;
+      const int64_t kv_first = cu_kv ? cu_kv[b] : cu_q[b];
+      const int64_t pos = n - L + (tok - cu_q[b]);
+      const int64_t r_row = (tok * Hq + h) * (int64_t)d_rel;
+      for (int d = 0; d < R; ++d) {
+        double acc = 0.0;
+        for (int kk = 0; kk < d_rel; ++kk)
+          acc += elem(r, dtype, r_row + kk) * elem(w, dtype, (int64_t)kk * R + d);
+        brow[d] = acc;
+      }
+      attend_row(dtype, q, (tok * Hq + h) * (int64_t)D, k, v,
+                 kv_first * (int64_t)Hkv * D, Hkv, D, h / G, pos, n, brow,
+                 ORC_F64, 0, R, W, sm_scale, scores, out + i * (int64_t)D,
+                 lse ? lse + i : NULL);
+    }
+    free(brow);
     free(scores);
   }
   return bad ? -1 : used;

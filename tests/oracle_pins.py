@@ -472,6 +472,113 @@ def pin_rejects_indivisible_heads(orc):
     raise AssertionError("indivisible head counts accepted")
 
 
+# --------------------------------------------------------------------------
+# the bias given by its projection, bias[t,h,d] = sum_k r[t,h,k] w[k,d]
+
+def _tiny_projected(seed, n_keys, n_new, Hq, Hkv, D, R, d_rel, dtype):
+    g = _gen(seed)
+    q = _rand((sum(n_new), Hq, D), g, dtype)
+    k = _rand((sum(n_keys), Hkv, D), g, dtype)
+    v = _rand((sum(n_keys), Hkv, D), g, dtype)
+    r = _rand((sum(n_new), Hq, d_rel), g, dtype, 0.7)
+    w = _rand((d_rel, R), g, dtype, 0.7)
+    return q, k, v, r, w
+
+
+def pin_brute_force_prefill_projected(orc):
+    """Rows and LSEs against pure-Python brute force whose bias row is the
+    fsum over k of r[t,h,k] w[k,d], with and without a cached history."""
+    cases = [
+        # n_keys, n_new (None: no history), Hq, Hkv, D, W, R, d_rel, dtype
+        ([6, 11], None, 4, 2, 3, 0, 4, 3, torch.float32),
+        ([9, 20], [3, 20], 2, 1, 4, 5, 7, 2, torch.bfloat16),
+        ([13], [13], 2, 2, 2, 0, 16, 5, torch.float32),
+    ]
+    for ci, (n_keys, n_new, Hq, Hkv, D, W, R, d_rel, dt) in enumerate(cases):
+        new = n_new if n_new is not None else n_keys
+        q, k, v, r, w = _tiny_projected(300 + ci, n_keys, new, Hq, Hkv, D, R, d_rel, dt)
+        scale = 0.41
+        out, lse = orc.prefill_projected(q, k, v, r, w, _cu(new),
+                                         _cu(n_keys) if n_new is not None else None,
+                                         window=W, sm_scale=scale, want_lse=True)
+        qd, kd, vd, rd, wd = _f64(q), _f64(k), _f64(v), _f64(r), _f64(w)
+        G = Hq // Hkv
+        tok, k0 = 0, 0
+        for n, L in zip(n_keys, new):
+            for i in range(L):
+                t = n - L + i
+                for h in range(Hq):
+                    g = h // G
+                    brow = [math.fsum(rd[tok, h, kk] * wd[kk, d] for kk in range(d_rel))
+                            for d in range(R)]
+                    keys = [list(kd[k0 + s, g]) for s in range(n)]
+                    vals = [list(vd[k0 + s, g]) for s in range(n)]
+                    ref, ref_lse = _brute_row(list(qd[tok, h]), keys, vals, brow, t, W, R, scale)
+                    err = np.max(np.abs(out[tok, h] - np.array(ref)))
+                    assert err < 1e-12, f"case {ci} tok {tok} h {h}: {err}"
+                    assert abs(lse[tok, h] - ref_lse) < 1e-12, f"lse case {ci}"
+                tok += 1
+            k0 += n
+
+
+def pin_projection_by_permutation(orc):
+    """w a permutation matrix (w[k, perm[k]] = 1): the bias row is r with its
+    columns permuted, bias[t,h,perm[k]] = r[t,h,k], so the result equals the
+    prefill given that tensor exactly.  perm is not an involution, so reading
+    w transposed gives a different row."""
+    n, Hq, D, R = 14, 2, 4, 6
+    perm = [2, 0, 5, 1, 3, 4]
+    g = _gen(41)
+    q, k, v = (_rand((n, Hq, D), g, torch.float32), _rand((n, 1, D), g, torch.float32),
+               _rand((n, 1, D), g, torch.float32))
+    r = _rand((n, Hq, R), g, torch.float32, 2.0)
+    w = torch.zeros((R, R))
+    for kk, d in enumerate(perm):
+        w[kk, d] = 1.0
+    b = torch.empty_like(r)
+    for kk, d in enumerate(perm):
+        b[:, :, d] = r[:, :, kk]
+    for W in (0, 5):
+        got = orc.prefill_projected(q, k, v, r, w, [0, 6, n], window=W, sm_scale=0.8)
+        ref = orc.prefill(q, k, v, b, [0, 6, n], window=W, rel_extent=R, sm_scale=0.8)
+        assert np.array_equal(got, ref), W
+
+
+def pin_projection_equal_columns_is_unbiased(orc):
+    """All columns of w equal: every bias row is one constant, which the
+    softmax cancels, so the result is attention without a bias."""
+    n, Hq, D, R, d_rel = 12, 2, 4, 5, 3
+    g = _gen(43)
+    q, k, v = (_rand((n, Hq, D), g, torch.float32), _rand((n, 2, D), g, torch.float32),
+               _rand((n, 2, D), g, torch.float32))
+    r = _rand((n, Hq, d_rel), g, torch.float32, 3.0)
+    w = _rand((d_rel, 1), g, torch.float32).expand(d_rel, R).contiguous()
+    got = orc.prefill_projected(q, k, v, r, w, [0, n], window=0, sm_scale=0.6)
+    ref = orc.prefill(q, k, v, torch.zeros((n, Hq, R)), [0, n], window=0, rel_extent=R,
+                      sm_scale=0.6)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def pin_projection_last_column_is_clamped_bucket(orc):
+    """r[t,h] = e_0 and w[0] = 50 in the last column only: every distance at
+    or beyond R-1 carries the bias, so query t averages keys 0 .. t-R+1."""
+    n, R, d_rel = 18, 4, 2
+    v = torch.randn((n, 1, 3))
+    q = torch.randn((n, 1, 3))
+    k = torch.zeros((n, 1, 3))
+    r = torch.zeros((n, 1, d_rel))
+    r[:, :, 0] = 1.0
+    w = torch.zeros((d_rel, R))
+    w[0, R - 1] = 50.0
+    w[1, 0] = 50.0          # never used: r[..., 1] = 0
+    out = orc.prefill_projected(q, k, v, r, w, [0, n], window=0, sm_scale=1.0)
+    vd = _f64(v)[:, 0]
+    for t in range(n):
+        far = t - (R - 1)
+        ref = vd[:far + 1].mean(axis=0) if far >= 0 else vd[:t + 1].mean(axis=0)
+        assert np.max(np.abs(out[t, 0] - ref)) < 1e-12, t
+
+
 ALL_PINS = [
     pin_brute_force_prefill,
     pin_brute_force_decode,
@@ -495,6 +602,10 @@ ALL_PINS = [
     pin_history_rows_of_full_prefill,
     pin_history_single_query_is_decode,
     pin_history_rejects_more_queries_than_keys,
+    pin_brute_force_prefill_projected,
+    pin_projection_by_permutation,
+    pin_projection_equal_columns_is_unbiased,
+    pin_projection_last_column_is_clamped_bucket,
 ]
 
 

@@ -19,14 +19,14 @@ ROOT = os.path.dirname(HERE)
 # (name, text in rba_oracle.c, replacement)
 MUTANTS = [
     ("bias dropped",
-     "scores[s] = sm_scale * dot + elem(bias, dtype, bias_row + d);",
-     "scores[s] = sm_scale * dot + 0.0 * elem(bias, dtype, bias_row + d);"),
+     "scores[s] = sm_scale * dot + elem(bias, bias_dtype, bias_row + d);",
+     "scores[s] = sm_scale * dot + 0.0 * elem(bias, bias_dtype, bias_row + d);"),
     ("bias scaled by sm_scale",
-     "scores[s] = sm_scale * dot + elem(bias, dtype, bias_row + d);",
-     "scores[s] = sm_scale * (dot + elem(bias, dtype, bias_row + d));"),
+     "scores[s] = sm_scale * dot + elem(bias, bias_dtype, bias_row + d);",
+     "scores[s] = sm_scale * (dot + elem(bias, bias_dtype, bias_row + d));"),
     ("distance read from the far end of the row",
-     "elem(bias, dtype, bias_row + d)",
-     "elem(bias, dtype, bias_row + (R - 1 - d))"),
+     "elem(bias, bias_dtype, bias_row + d)",
+     "elem(bias, bias_dtype, bias_row + (R - 1 - d))"),
     ("clamp to the wrong bucket",
      "if (d > R - 1) d = R - 1;",
      "if (d > R - 1) d = (R > 1 ? R - 2 : 0);"),
@@ -57,6 +57,18 @@ MUTANTS = [
     ("history queries placed at the start of the sequence",
      "const int64_t pos = n - L + (tok - cu_q[b]);",
      "const int64_t pos = tok - cu_q[b];"),
+    ("projection reads w transposed",
+     "acc += elem(r, dtype, r_row + kk) * elem(w, dtype, (int64_t)kk * R + d);",
+     "acc += elem(r, dtype, r_row + kk) * elem(w, dtype, (int64_t)d * d_rel + kk);"),
+    ("projection drops its last term",
+     "for (int kk = 0; kk < d_rel; ++kk)",
+     "for (int kk = 0; kk < d_rel - 1; ++kk)"),
+    ("projected bias row of the neighbouring head",
+     "const int64_t r_row = (tok * Hq + h) * (int64_t)d_rel;",
+     "const int64_t r_row = (tok * Hq + (h + 1) % Hq) * (int64_t)d_rel;"),
+    ("projected rows ignore the history",
+     "const int64_t pos = n - L + (tok - cu_q[b]);\n      const int64_t r_row",
+     "const int64_t pos = tok - cu_q[b];\n      const int64_t r_row"),
     ("no max subtraction lost in normalisation",
      "for (int i = 0; i < D; ++i) out[i] /= l;",
      "for (int i = 0; i < D; ++i) out[i] /= (l + 1e-3);"),
