@@ -29,7 +29,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MAIN = "local-prefill-4x4096"
 SECONDARY = ["global-prefill-2x16384", "mixed-decode-256", "long-decode-32x131072",
-             "chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384", "kv-append-8x2048"]
+             "chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384", "kv-append-8x2048",
+             "fused-local-prefill-4x4096-drel32", "fused-global-prefill-2x16384-drel32"]
 RIDGE_FLOP_PER_BYTE = 315.0
 
 
@@ -78,6 +79,26 @@ def prefill_history_work(case):
     T = case.total_tokens
     flops = 4 * D * Hq * pairs
     byt = T * Hq * D * es * 2 + kv_keys * Hkv * D * es * 2 + Hq * es * bias_entries
+    return flops, byt
+
+
+def prefill_projected_work(case):
+    """Prefill with the bias formed from its projection: the attention of
+    prefill_history_work, plus 2*d_rel FLOPs per bias entry a row uses; the
+    bias bytes become those of r [T, Hq, d_rel] and W [d_rel, R]."""
+    h = case.hist
+    sp = h.spec
+    es = 2
+    flops, byt = prefill_history_work(h)
+    bias_entries = 0
+    W, R = sp.window, sp.rel_extent
+    for n, L in zip(h.key_lens, h.new_lens):
+        for p in range(n - L, n):
+            vis = min(p + 1, W) if W > 0 else p + 1
+            bias_entries += min(vis, R)
+    byt -= sp.num_q_heads * es * bias_entries
+    byt += case.rel_r.numel() * es + case.w_rel.numel() * es
+    flops += 2 * case.d_rel * sp.num_q_heads * bias_entries
     return flops, byt
 
 
@@ -198,6 +219,19 @@ def run_prefill(case, steps, warmup, torch, rba):
     return time_steps(step, steps, warmup, torch)
 
 
+def run_prefill_fused(case, steps, warmup, torch, rba):
+    h = case.hist
+    sp = h.spec
+    out = torch.empty_like(h.q)
+
+    def step():
+        rba.prefill_fused(h.q, h.cu_seqlens, h.max_seqlen, h.k_pool, h.v_pool, h.block_table,
+                          h.seq_lens_dev, case.rel_r, case.w_rel_t, window=sp.window,
+                          sm_scale=sp.scale(), out=out)
+
+    return time_steps(step, steps, warmup, torch)
+
+
 def run_decode(cases, splits, steps, warmup, torch, rba):
     ws = {}
     outs = {}
@@ -238,13 +272,18 @@ def secondary(name, torch, rba, ri, steps, warmup):
                 "algorithmic_bytes": byt,
                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
-    if w["kind"] in ("prefill", "prefill-history"):
+    if w["kind"] in ("prefill", "prefill-history", "prefill-projected"):
         case = cases["prefill"]
-        flops, byt = (prefill_work if w["kind"] == "prefill" else prefill_history_work)(case)
-        wall, ev = run_prefill(case, steps, warmup, torch, rba)
+        work = {"prefill": prefill_work, "prefill-history": prefill_history_work,
+                "prefill-projected": prefill_projected_work}[w["kind"]]
+        flops, byt = work(case)
+        if w["kind"] == "prefill-projected":
+            wall, ev = run_prefill_fused(case, steps, warmup, torch, rba)
+        else:
+            wall, ev = run_prefill(case, steps, warmup, torch, rba)
         tf = flops / (ev * 1e-3) / 1e12
         gbs = byt / (ev * 1e-3) / 1e9
-        if w["kind"] == "prefill-history" and flops / byt < RIDGE_FLOP_PER_BYTE:
+        if w["kind"] != "prefill" and flops / byt < RIDGE_FLOP_PER_BYTE:
             roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
         else:
@@ -339,11 +378,17 @@ def main():
                                     algorithmic_bytes=res["algorithmic_bytes"]))
         print(json.dumps(result), flush=True)
         return
-    if w["kind"] == "prefill-history":
+    if w["kind"] in ("prefill-history", "prefill-projected"):
         res = secondary(args.workload, torch, rba, ri, args.steps, args.warmup)
+        fused = w["kind"] == "prefill-projected"
+        kernel = ("prefill_bf16_kernel<128, 8 waves, d_rel 32> (bias formed in the kernel)" if fused
+                  else "prefill_bf16_kernel<128>")
         result = dict(base, value=res["value"], unit="TFLOP/s", ms_per_step=res["ms_per_step"],
                       config={"workload": args.workload, "parallelism": "single GPU"},
-                      roofline=dict(res["roofline"], traffic=None, kernel="prefill_bf16_kernel<128>",
+                      roofline=dict(res["roofline"],
+                                    traffic=(recorded_traffic(args.workload, "prefill_bf16.hip")
+                                             if fused else None),
+                                    kernel=kernel,
                                     kernel_ms=res["kernel_ms"],
                                     algorithmic_bytes=res["algorithmic_bytes"],
                                     algorithmic_flops=res["algorithmic_flops"]))

@@ -147,6 +147,33 @@ rba_status rba_prefill(const void *q, const int32_t *cu_seqlens,
                        void *out, float *lse, hipStream_t stream);
 
 /*
+ * Prefill with the bias formed on the fly from its projection instead of
+ * read from a [T][Hq][R] tensor:
+ *   bias[t,h,d] = sum_k rel_r[t,h,k] * W[k,d],   d = 0 .. R-1,
+ * the product the TensorRT-LLM PR #17062 page's review comment on
+ * _build_rel_logits materialises per layer (r [T, heads, d_rel] times
+ * rel_logits_proj [d_rel, rel_extent]); everything else as rba_prefill.
+ * The products are accumulated in fp32 from the bf16 inputs and rounded
+ * to bf16 before they join the score (the page's fp32 tensor, emitted in
+ * bf16 as its review suggests); the clamped bucket d = R-1 of distances at
+ * or beyond R-1 stays in fp32.
+ *
+ *  rel_r    bf16 [total_tokens][Hq][d_rel], 16-byte aligned
+ *  w_rel_t  bf16 [rel_extent][d_rel]: W transposed (distance-major),
+ *           16-byte aligned; a weight, laid out once
+ *  d_rel    16 or 32 (the pages leave it open)
+ *
+ * bf16 pools only.  Errors as rba_prefill, plus RBA_ERR_INVALID_ARG for
+ * d_rel <= 0 and RBA_ERR_UNSUPPORTED for an fp32 pool or another d_rel.
+ */
+rba_status rba_prefill_fused(const void *q, const int32_t *cu_seqlens,
+                             int32_t total_tokens, int32_t max_seqlen,
+                             const rba_kv_cache *kv, const rba_page_table *pt,
+                             const void *rel_r, const void *w_rel_t,
+                             int32_t d_rel, const rba_attn_params *params,
+                             void *out, float *lse, hipStream_t stream);
+
+/*
  * Number of key-range partitions rba_decode will use for these arguments
  * (num_splits == 0 picks one from the host bound max_seq_len; otherwise the
  * requested count, capped at 256).  Returns 0 on invalid arguments.

@@ -229,10 +229,10 @@ def _cumsum(lens):
 
 def make_prefill_history(spec: LayerSpec, key_lens: List[int], new_lens: List[int], seed: int,
                          device="cpu", num_pages: Optional[int] = None,
-                         shuffle: bool = True) -> HistoryCase:
+                         shuffle: bool = True, with_bias: bool = True) -> HistoryCase:
     """Prefill inputs over a history: all key_lens[b] keys of each sequence
     are in shuffled pool pages; queries and bias rows exist for the last
-    new_lens[b] positions only."""
+    new_lens[b] positions only (with_bias False: no bias tensor)."""
     if any(m > n for m, n in zip(new_lens, key_lens)):
         raise ValueError("more new tokens than keys")
     P = spec.page_size
@@ -241,8 +241,8 @@ def make_prefill_history(spec: LayerSpec, key_lens: List[int], new_lens: List[in
     q = _randn((int(sum(new_lens)), spec.num_q_heads, spec.head_dim), g, device, spec.dtype)
     k_log = _randn((int(sum(key_lens)), spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
     v_log = _randn((int(sum(key_lens)), spec.num_kv_heads, spec.head_dim), g, device, spec.dtype)
-    bias = _randn((int(sum(new_lens)), spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
-                  std=spec.bias_std)
+    bias = (_randn((int(sum(new_lens)), spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
+                   std=spec.bias_std) if with_bias else None)
     pages_per = [max(1, -(-n // P)) for n in key_lens]
     needed = int(sum(pages_per))
     if num_pages is None:
@@ -271,6 +271,41 @@ def make_prefill_history(spec: LayerSpec, key_lens: List[int], new_lens: List[in
         cu_seqlens=torch.tensor(_cumsum(new_lens), dtype=torch.int32, device=device),
         seq_lens_dev=torch.tensor(list(key_lens) or [0], dtype=torch.int32, device=device)[:B],
         block_table=table.to(device), k_pool=k_pool, v_pool=v_pool)
+
+
+@dataclasses.dataclass
+class ProjectedCase:
+    """Prefill whose bias is given by its projection: rel_r [sum new, Hq,
+    d_rel] and w_rel [d_rel, R] (w_rel_t = its transpose, the layout the
+    fused kernel reads).  ``hist`` holds everything else (its bias is None)."""
+    hist: HistoryCase
+    rel_r: torch.Tensor
+    w_rel: torch.Tensor
+    w_rel_t: torch.Tensor
+
+    @property
+    def spec(self) -> LayerSpec:
+        return self.hist.spec
+
+    @property
+    def d_rel(self) -> int:
+        return int(self.w_rel.shape[0])
+
+
+def make_projected(spec: LayerSpec, key_lens: List[int], new_lens: Optional[List[int]],
+                   d_rel: int, seed: int, device="cpu", num_pages: Optional[int] = None,
+                   r_std: float = 1.0) -> ProjectedCase:
+    """Inputs of the fused prefill.  r ~ N(0, r_std^2) and W ~ N(0, (bias_std /
+    (r_std sqrt(d_rel)))^2), so the bias r . W has the spread bias_std of the
+    stored bias tensors; new_lens None: no history (every key is a query)."""
+    new = list(key_lens) if new_lens is None else list(new_lens)
+    hist = make_prefill_history(spec, list(key_lens), new, seed, device=device,
+                                num_pages=num_pages, with_bias=False)
+    g = _dev_gen(seed + 7919, device)
+    rel_r = _randn((int(sum(new)), spec.num_q_heads, d_rel), g, device, spec.dtype, std=r_std)
+    w_rel = _randn((d_rel, spec.rel_extent), g, device, spec.dtype,
+                   std=spec.bias_std / (r_std * math.sqrt(d_rel)))
+    return ProjectedCase(hist=hist, rel_r=rel_r, w_rel=w_rel, w_rel_t=w_rel.t().contiguous())
 
 
 @dataclasses.dataclass
@@ -413,6 +448,15 @@ WORKLOADS = {
     "chunked-global-2x2048-ctx16384": dict(
         kind="prefill-history", seed=1007, key_lens=[16384] * 2, new_lens=[2048] * 2,
         num_pages=512, spec=LayerSpec(**GLOBAL)),
+    # the two prefill layers with the bias formed from its projection
+    # r [T, Hq, d_rel] . W [d_rel, R] in the kernel (d_rel is not stated on
+    # the pages; 32 here)
+    "fused-local-prefill-4x4096-drel32": dict(
+        kind="prefill-projected", seed=1009, seq_lens=[4096] * 4, num_pages=512, d_rel=32,
+        spec=LayerSpec(**LOCAL)),
+    "fused-global-prefill-2x16384-drel32": dict(
+        kind="prefill-projected", seed=1010, seq_lens=[16384] * 2, num_pages=512, d_rel=32,
+        spec=LayerSpec(**GLOBAL)),
 }
 
 
@@ -435,6 +479,9 @@ def build_workload(name: str, device="cpu"):
     if w["kind"] == "prefill-history":
         return {"prefill": make_prefill_history(w["spec"], w["key_lens"], w["new_lens"], w["seed"],
                                                 device, num_pages=w["num_pages"])}
+    if w["kind"] == "prefill-projected":
+        return {"prefill": make_projected(w["spec"], w["seq_lens"], None, w["d_rel"], w["seed"],
+                                          device, num_pages=w["num_pages"])}
     if w["kind"] == "mixed-decode":
         lens = mixed_decode_lengths(w["seed"], w["batch"], w["ctx_lo"], w["ctx_hi"])
         return {

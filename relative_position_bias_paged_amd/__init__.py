@@ -32,7 +32,7 @@ RBA_BF16 = 0
 RBA_F32 = 1
 
 # every symbol include/rba.h declares
-EXPORTED = ("rba_prefill", "rba_decode", "rba_decode_num_splits",
+EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_num_splits",
             "rba_decode_workspace_size", "rba_kv_append", "rba_window_ring_pages",
             "rba_status_string")
 
@@ -90,6 +90,12 @@ def load():
                                 P(rba_attn_params), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p]
     lib.rba_prefill.restype = ctypes.c_int
+    lib.rba_prefill_fused.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_int32, P(rba_kv_cache), P(rba_page_table),
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      P(rba_attn_params), ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.rba_prefill_fused.restype = ctypes.c_int
     lib.rba_decode.argtypes = [ctypes.c_void_p, P(rba_kv_cache), P(rba_page_table), ctypes.c_int32,
                                ctypes.c_void_p, P(rba_attn_params), ctypes.c_int32,
                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
@@ -197,6 +203,45 @@ def prefill(q: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
                          _dev(bias, "bias"), ctypes.byref(prm), _dev(out, "out"), lse_ptr,
                          _stream(stream))
     _check(st, "rba_prefill")
+    return out
+
+
+def prefill_fused(q: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                  k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor,
+                  seq_lens: Optional[torch.Tensor], rel_r: torch.Tensor, w_rel_t: torch.Tensor,
+                  *, window: int, sm_scale: float, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rba_prefill_fused: the bias formed in the kernel from rel_r [T,Hq,d_rel] and
+    w_rel_t [R,d_rel] (W transposed); returns out [T,Hq,D]."""
+    lib = load()
+    if q.dim() != 3 or rel_r.dim() != 3 or rel_r.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [T,Hq,D] and rel_r [T,Hq,d_rel]")
+    if w_rel_t.dim() != 2 or w_rel_t.shape[1] != rel_r.shape[2]:
+        raise ValueError("w_rel_t must be [R, d_rel] with the d_rel of rel_r")
+    T, hq, hd = q.shape
+    R, d_rel = w_rel_t.shape
+    kv, pt, prm = _structs(k_pool, v_pool, block_table, seq_lens, hq, window, R, sm_scale)
+    for name, t in (("q", q), ("rel_r", rel_r), ("w_rel_t", w_rel_t)):
+        if t.dtype != k_pool.dtype:
+            raise TypeError(f"{name} and the pools must share one dtype")
+    if hd != k_pool.shape[3]:
+        raise ValueError("head_dim of q and pools differ")
+    if cu_seqlens.numel() != block_table.shape[0] + 1:
+        raise ValueError("cu_seqlens must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lse_ptr = None
+    if lse is not None:
+        if lse.shape != (T, hq):
+            raise ValueError("lse must be [T, Hq]")
+        lse_ptr = _dev(lse, "lse", torch.float32)
+    st = lib.rba_prefill_fused(_dev(q, "q"), _dev(cu_seqlens, "cu_seqlens", torch.int32), T,
+                               int(max_seqlen), ctypes.byref(kv), ctypes.byref(pt),
+                               _dev(rel_r, "rel_r"), _dev(w_rel_t, "w_rel_t"), int(d_rel),
+                               ctypes.byref(prm), _dev(out, "out"), lse_ptr, _stream(stream))
+    _check(st, "rba_prefill_fused")
     return out
 
 

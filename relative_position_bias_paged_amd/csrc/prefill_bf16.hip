@@ -41,6 +41,17 @@
 //    sequence or in masked positions cannot leak into the output;
 //  * the running max is rescaled lazily (only when a row's max grows by more
 //    than 2^8), which is exact because numerator and denominator share it.
+//
+// The fused variant (DR = d_rel > 0) takes no bias tensor: it forms
+// bias[t,h,d] = r[t,h,:] . W[:,d] on the fly, the product that page's review
+// comment on _build_rel_logits materialises as [T, heads, rel_extent] (there
+// in fp32).  Per tile the work-group loads, with K and V, the rows of W^T
+// ([R][d_rel], distance-major) for the distances its queries meet, clamped to
+// [0, R-1]; each wave with a band tile multiplies them by its 32 r rows on the
+// matrix cores (3 x d_rel/16 MFMAs give the 96 distances of its 32 queries),
+// rounds the products to bf16 and writes them skewed into its stage, so that
+// the same aligned stage reads as above hand each lane its four runs.  Tiles
+// at or beyond R-1 use r . W[:,R-1], formed once per row in fp32.
 #include "rba_internal.h"
 
 #include <climits>
@@ -115,8 +126,19 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
 // 11:8) that waits for LDS and scalar memory traffic only.
 constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
 
-template <int D, int NW, bool BIG_PAGE, bool VEC_BIAS>
+// Fused stage layout: row q of a wave's stage starts at element 32 + 96*q and
+// holds distance index e (0..63 in use) at +e.  The product for distance
+// index idx = e + q of query q is written at 32 + 95*q + idx, so a lane's
+// writes sit at fixed offsets from one per-lane base; the indices it also
+// computes outside 0..63 (-31..95) land in the unused elements 64..95 of its
+// own or the previous row, or in the 32-element head.
+constexpr int FUSED_ROW = 96;
+constexpr int FUSED_STAGE = 32 + 32 * FUSED_ROW;
+
+template <int D, int NW, bool BIG_PAGE, bool VEC_BIAS, int DR>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr bool FUSED = DR > 0;                // bias formed from r and W^T
+  static_assert(!FUSED || (NW == 8 && (DR == 16 || DR == 32)), "fused variant: 8 waves, d_rel 16 or 32");
   constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
   constexpr int KB = D / 16;                    // MFMA k-steps over head_dim
   constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
@@ -127,8 +149,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
   __shared__ __align__(16) uint16_t k_lds1[BN * D], v_lds1[BN * D];
   // bias stage: per wave, 32 rows x 64 distances, 16-byte chunks of row r
-  // XOR-swizzled by (r/2) mod 8 so the lanes' aligned reads avoid bank conflicts
-  __shared__ __align__(16) uint16_t bias_stage[NW * 32 * BN];
+  // XOR-swizzled by (r/2) mod 8 so the lanes' aligned reads avoid bank
+  // conflicts (fused variant: the skewed layout above, unswizzled)
+  constexpr int STAGE_W = FUSED ? FUSED_STAGE : 32 * BN;
+  __shared__ __align__(16) uint16_t bias_stage[NW * STAGE_W];
+  // fused variant: two buffers of W^T rows (distances P0-s0-63 .. P0+QM-1-s0
+  // of tile s0, P0 the work-group's first query position), at most 32*NW+64
+  // rows of DR elements
+  constexpr int WSL_ROWS = 32 * NW + 64;
+  uint16_t *wsl0 = nullptr, *wsl1 = nullptr;
+  if constexpr (FUSED) {
+    __shared__ __align__(16) uint16_t w_sl0[WSL_ROWS * DR], w_sl1[WSL_ROWS * DR];
+    wsl0 = w_sl0;
+    wsl1 = w_sl1;
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -197,6 +231,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // a layer whose window stays within the R buckets never sees a clamped
   // distance inside its window
   const bool wide_layer = W <= 0 || W > R;
+  // The same tests as single unsigned range compares, s0 - lo - 1 < span
+  // (tiles are never below 0, so lower bounds under -1 are clamped to -1):
+  //   active     lo = max(s_lo, -1),        up to s_hi
+  //   band       lo = max(s_lo, s_band, -1), up to s_hi (active and band)
+  //   path 0     lo = max(s_wedge, -1), up to min(s_diag, s_tail, s_band):
+  //              active, unmasked and clamp-only
+  const int act_lo = max(s_lo, -1);
+  const uint32_t act_span = (uint32_t)(s_hi - act_lo);
+  const int band_lo = max(max(s_lo, s_band), -1);
+  const uint32_t band_span = (uint32_t)max(s_hi - band_lo, 0);
+  const int p0_lo = max(s_wedge, -1);
+  const uint32_t p0_span = (uint32_t)max(min(min(s_diag, s_tail), s_band) - p0_lo, 0);
+  auto in_range = [](int s0, int lo, uint32_t span) { return (uint32_t)(s0 - lo - 1) < span; };
 
   const uint16_t *qp = static_cast<const uint16_t *>(a.q);
   const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
@@ -228,11 +275,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // either end of it: waves holding such a row read element by element with
   // distances clamped to [0, R) instead.  Values read outside [0, R) are
   // masked or replaced by the clamped bucket.
-  const uint16_t *brow = static_cast<const uint16_t *>(a.bias) + row * R;
-  const float b_last = bf16_to_f32(brow[R - 1]);
-  const long long row_off = (long long)row * R;
-  const long long bias_elems = (long long)a.total_tokens * Hq * R;
-  const bool edge_wave = __ballot(row_off < 1024 || bias_elems - row_off < R + 1024) != 0;
+  //
+  // Fused variant: this lane's B operand of the bias product, r[row] in
+  // k-steps of 16 (lane half `half` holds elements 8*half .. 8*half+7 of
+  // each), and the clamped bucket r[row] . W[:,R-1] formed in fp32.
+  const uint16_t *brow = nullptr;
+  float b_last;
+  bool edge_wave;
+  u32x4_t rf[FUSED ? DR / 16 : 1];
+  if constexpr (FUSED) {
+    const uint16_t *rp = static_cast<const uint16_t *>(a.rel_r);
+    const uint16_t *wlast = static_cast<const uint16_t *>(a.w_rel_t) + (size_t)(R - 1) * DR;
+    float part = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < DR / 16; ++kk) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(rp + row * DR + kk * 16 + half * 8);
+      rf[kk] = row_ok ? v : u32x4_t{0, 0, 0, 0};
+      const u32x4_t w = *reinterpret_cast<const u32x4_t *>(wlast + kk * 16 + half * 8);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) part = fmaf(bf16x8_elem(rf[kk], x), bf16x8_elem(w, x), part);
+    }
+    b_last = part + __shfl_xor(part, 32);
+    edge_wave = false;
+  } else {
+    brow = static_cast<const uint16_t *>(a.bias) + row * R;
+    b_last = bf16_to_f32(brow[R - 1]);
+    const long long row_off = (long long)row * R;
+    const long long bias_elems = (long long)a.total_tokens * Hq * R;
+    edge_wave = __ballot(row_off < 1024 || bias_elems - row_off < R + 1024) != 0;
+  }
 
   // ---- K/V tile loads, global -> LDS -------------------------------------
   // Write j of this wave fills LDS rows (DMA_PER_WAVE*wave + j)*ROWS_PER_DMA
@@ -290,8 +361,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // t - s0 - 8*half - 16*p - 7 .. t - s0 - 8*half - 16*p in ascending order,
   // i.e. the keys s0 + 32*sub + 16*G + 8*half + 7 down to + 0: chunk
   // 7 - half - 2p of the row's 64 staged distances t - s0 - 63 .. t - s0.
-  const bool use_stage = VEC_BIAS && !edge_wave;
-  uint16_t *stage_w = bias_stage + wave * (32 * BN);
+  const bool use_stage = FUSED || (VEC_BIAS && !edge_wave);
+  uint16_t *stage_w = bias_stage + wave * STAGE_W;
   // Stage write k of this lane: row 8k + lane/8 of the wave, physical chunk
   // lane%8 = logical chunk c ^ swizzle.  Pointer for tile 0; tile s0 is
   // s0 elements lower.
@@ -310,7 +381,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     for (int k = 0; k < 4; ++k) dma16(sptr[k] - 2 * (long long)s0, (lds_void_t *)(stage_w + k * 512));
   };
   auto load_bias = [&](int s0, u32x4_t (&bp)[4]) {
-    if (use_stage) {
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        bp[p] = *reinterpret_cast<const u32x4_t *>(stage_w + 32 + col * FUSED_ROW + (7 - half - 2 * p) * 8);
+    } else if (use_stage) {
       const int sw = (col >> 1) & 7;
 #pragma unroll
       for (int p = 0; p < 4; ++p)
@@ -326,6 +401,61 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
           v[x >> 1] |= (uint32_t)brow[d] << ((x & 1) * 16);
         }
         bp[p] = v;
+      }
+    }
+  };
+
+  // ---- fused variant: W^T rows and the bias product ---------------------------
+  // The W^T buffer of tile s0 holds rows d0 .. d0 + QM + 63 of W^T, clamped to
+  // [0, R-1], with d0 = P0 - s0 - 63 the smallest distance of the work-group's
+  // first query P0 (finite values for distances below 0, which are masked).
+  // Wave (query block qb) reads rows 32*qb .. 32*qb + 95: distance index idx
+  // of its query q is distance pq0 + q - s0 - 63 + (idx - q).
+  const int P0 = hist + t0;
+  // some wave of the work-group reads bias for tile s0: the first query
+  // block (qb = 0, queries from P0) meets the smallest distances
+  auto wg_band = [&](int s0) { return s0 > P0 - (BN - 2) - R; };
+  auto load_wslice = [&](int s0, uint16_t *dst) {
+    if constexpr (FUSED) {
+      constexpr int LPR = DR / 8;        // lanes per W^T row (16 bytes each)
+      constexpr int RPI = 64 / LPR;      // rows per 1 KiB direct load
+      const uint16_t *wt = static_cast<const uint16_t *>(a.w_rel_t);
+      const int n_ld = (QM + 64) / RPI;
+      const int d0 = P0 - s0 - (BN - 1);
+      for (int i = wave; i < n_ld; i += NW) {
+        const int dd = min(max(d0 + i * RPI + lane / LPR, 0), R - 1);
+        dma16(wt + (size_t)dd * DR + (lane % LPR) * 8, (lds_void_t *)(dst + i * 512));
+      }
+    }
+  };
+  // Bias of tile s0 for this wave's 32 queries into its stage: C^T = W^T r^T
+  // over 96 distance indices in three 32-row MFMA blocks (A = W^T rows from
+  // the buffer, B = r), rounded to bf16.  Register 4i+j of block b holds
+  // index idx = 32b + 8i + 4*half + j of query col, written at
+  // 32 + 95*col + idx of the stage.
+  auto fuse_bias = [&](const uint16_t *wsl) {
+    if constexpr (FUSED) {
+      const uint16_t *wa = wsl + (32 * qb + col) * DR + half * 8;
+      uint16_t *sb = stage_w + 32 + (FUSED_ROW - 1) * col + 4 * half;
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        f32x16_t acc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < DR / 16; ++kk) {
+          const u32x4_t w = *reinterpret_cast<const u32x4_t *>(wa + 32 * b * DR + kk * 16);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w),
+                                                        __builtin_bit_cast(bf16x8_t, rf[kk]), acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; j += 2) {
+            const uint32_t pk = pack_bf16x2(acc[4 * i + j], acc[4 * i + j + 1]);
+            sb[32 * b + 8 * i + j] = (uint16_t)pk;
+            sb[32 * b + 8 * i + j + 1] = (uint16_t)(pk >> 16);
+          }
       }
     }
   };
@@ -359,16 +489,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int vbase = vrow * D + (vi & 1) * 4;
 
   auto compute_tile = [&](int s0, const uint16_t *kl, const uint16_t *vl, const u32x4_t (&bp)[4]) {
-    if (s0 > s_hi || s0 <= s_lo) return;       // no key of the tile is visible to this wave
+    const bool fixed0 = in_range(s0, p0_lo, p0_span);   // clamp-only, unmasked
+    if (!fixed0 && !in_range(s0, act_lo, act_span)) return;   // no key of the tile is visible
     const bool need_mask = s0 > s_diag || s0 <= s_wedge || s0 > s_tail;
     const bool band = s0 > s_band;
     const bool beyond = s0 <= s_strad;         // some distance exceeds R-1
     // score path: 0 clamp-only unmasked, 1 band unmasked, 2 general (a band
     // tile with a visible distance beyond R-1 is one of the edges)
-    const int path = (!need_mask && !band) ? 0 : ((!need_mask && !(beyond && wide_layer)) ? 1 : 2);
-    // no visible key of this wave lies beyond distance R-1 (a windowed layer
-    // with window <= R, or a band tile that does not reach R-1): the staged
-    // bias serves every key of a path-2 tile
+    const int path = fixed0 ? 0 : ((!need_mask && !(beyond && wide_layer)) ? 1 : 2);
     const bool clamp_free = band && (!wide_layer || !beyond);
     // exp2 argument = fma(v, sa, sb - m2): v is the raw q.k on path 0 (scale
     // and the clamped bias folded into sa, sb), the finished score otherwise
@@ -517,7 +645,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // have copied tile i's runs out of it); the barrier closing tile i waits
   // for both.  Unrolled by two so each buffer is fixed at compile time.
   auto wave_band = [&](int s0) {      // this wave computes tile s0 and reads its bias
-    return s0 <= s_hi && s0 > s_lo && s0 > s_band;
+    return in_range(s0, band_lo, band_span);
   };
 
   u32x4_t bias_r[4] = {zero4, zero4, zero4, zero4};
@@ -552,14 +680,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   int steps_left = n_t;
   // One step: bias runs of tile s_cur into registers, then the loads of
   // s_nxt (unless s_cur is the last), then the compute of s_cur.
-  auto step = [&](uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, int &page_nxt) {
+  // (Fused variant: the bias product of tile s_cur goes into the stage first,
+  // from the W^T buffer loaded with the tile; the W^T rows of s_nxt load with
+  // its K/V into the other buffer.)
+  auto step = [&](uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, const uint16_t *wc,
+                  uint16_t *wn, int &page_nxt) {
     const int s0 = s_cur;
     const bool more = --steps_left > 0;
-    if (wave_band(s0)) load_bias(s0, bias_r);
+    if (wave_band(s0)) {
+      fuse_bias(wc);
+      load_bias(s0, bias_r);
+    }
     if (more) {
       load_kv(s_nxt, page_nxt, kn, vn);
       page_nxt = tile_page(s_nxt2);
-      if (use_stage && wave_band(s_nxt)) {
+      if constexpr (FUSED) {
+        if (wg_band(s_nxt)) load_wslice(s_nxt, wn);
+      } else if (use_stage && wave_band(s_nxt)) {
         // the stage is rewritten: this lane's reads of it must be done
         __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
         stage_bias(s_nxt);
@@ -574,13 +711,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   };
 
   load_kv(s_cur, tile_page(s_cur), k_lds0, v_lds0);
-  if (use_stage && wave_band(s_cur)) stage_bias(s_cur);
+  if constexpr (FUSED) {
+    if (wg_band(s_cur)) load_wslice(s_cur, wsl0);
+  } else if (use_stage && wave_band(s_cur)) {
+    stage_bias(s_cur);
+  }
   int page_nxt = tile_page(s_nxt);
   __syncthreads();
 
   for (;;) {
-    if (!step(k_lds0, v_lds0, k_lds1, v_lds1, page_nxt)) break;
-    if (!step(k_lds1, v_lds1, k_lds0, v_lds0, page_nxt)) break;
+    if (!step(k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt)) break;
+    if (!step(k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt)) break;
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -609,10 +750,17 @@ static void launch_d(const PrefillArgs &a, hipStream_t s) {
   dim3 grid(a.num_blocks), block(64 * NW);
   const bool big = a.page_size >= BN;
   const bool vec = a.R >= 8;
-  if (big && vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, true>), grid, block, 0, s, a);
-  else if (big) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, false>), grid, block, 0, s, a);
-  else if (vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, false>), grid, block, 0, s, a);
+  if (big && vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, true, 0>), grid, block, 0, s, a);
+  else if (big) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, false, 0>), grid, block, 0, s, a);
+  else if (vec) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, true, 0>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, false, 0>), grid, block, 0, s, a);
+}
+
+template <int D, int DR>
+static void launch_fused_d(const PrefillArgs &a, hipStream_t s) {
+  dim3 grid(a.num_blocks), block(64 * 8);
+  if (a.page_size >= BN) hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, true, true, DR>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, false, true, DR>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
@@ -623,6 +771,20 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s
   } else if (head_dim == 64) {
     if (a.waves == 8) launch_d<64, 8>(a, s);
     else launch_d<64, 4>(a, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_fused(const PrefillArgs &a, int head_dim, hipStream_t s) {
+  if (a.waves != 8 || (a.d_rel != 16 && a.d_rel != 32)) return hipErrorInvalidValue;
+  if (head_dim == 128) {
+    if (a.d_rel == 32) launch_fused_d<128, 32>(a, s);
+    else launch_fused_d<128, 16>(a, s);
+  } else if (head_dim == 64) {
+    if (a.d_rel == 32) launch_fused_d<64, 32>(a, s);
+    else launch_fused_d<64, 16>(a, s);
   } else {
     return hipErrorInvalidValue;
   }

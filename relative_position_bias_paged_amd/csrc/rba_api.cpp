@@ -123,19 +123,25 @@ RBA_EXPORT const char *rba_status_string(rba_status status) {
   return "RBA_UNKNOWN_STATUS";
 }
 
-RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int32_t total_tokens,
-                                  int32_t max_seqlen, const rba_kv_cache *kv,
-                                  const rba_page_table *pt, const void *bias,
-                                  const rba_attn_params *params, void *out, float *lse,
-                                  hipStream_t stream) {
+namespace {
+
+// Shared by rba_prefill (bias tensor given) and rba_prefill_fused (bias
+// formed from rel_r and w_rel_t, d_rel > 0).
+rba_status prefill_impl(const void *q, const int32_t *cu_seqlens, int32_t total_tokens,
+                        int32_t max_seqlen, const rba_kv_cache *kv, const rba_page_table *pt,
+                        const void *bias, const void *rel_r, const void *w_rel_t, int32_t d_rel,
+                        const rba_attn_params *params, void *out, float *lse, hipStream_t stream) {
+  const bool fused = d_rel != 0;
   rba_status st = check_layer(kv, pt, params);
   if (st != RBA_OK) return st;
-  if (total_tokens < 0 || max_seqlen < 0) return RBA_ERR_INVALID_ARG;
+  if (total_tokens < 0 || max_seqlen < 0 || d_rel < 0) return RBA_ERR_INVALID_ARG;
+  if (fused && (kv->dtype != RBA_BF16 || (d_rel != 16 && d_rel != 32))) return RBA_ERR_UNSUPPORTED;
   if (total_tokens == 0 || pt->num_seqs == 0 || max_seqlen == 0) return RBA_OK;
-  if (q == nullptr || cu_seqlens == nullptr || bias == nullptr || out == nullptr)
+  if (q == nullptr || cu_seqlens == nullptr || out == nullptr) return RBA_ERR_INVALID_ARG;
+  if (fused ? (rel_r == nullptr || w_rel_t == nullptr || !aligned16(rel_r) || !aligned16(w_rel_t))
+            : (bias == nullptr || !aligned16(bias)))
     return RBA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(bias) || !aligned16(out) || !pool_ok(kv, pt))
-    return RBA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(out) || !pool_ok(kv, pt)) return RBA_ERR_INVALID_ARG;
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
   if ((long long)max_seqlen > (long long)pt->max_pages_per_seq * pt->page_size)
     return RBA_ERR_INVALID_ARG;
@@ -147,7 +153,10 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
   a.v_pool = kv->v_pool;
   a.block_table = pt->block_table;
   a.seq_lens = pt->seq_lens;       // null: the queries are all the keys
-  a.bias = bias;
+  a.bias = fused ? nullptr : bias;
+  a.rel_r = fused ? rel_r : nullptr;
+  a.w_rel_t = fused ? w_rel_t : nullptr;
+  a.d_rel = d_rel;
   a.out = out;
   a.lse = lse;
   a.num_seqs = pt->num_seqs;
@@ -166,7 +175,8 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
   if (kv->dtype == RBA_BF16) {
     // Query heads of one KV head share a work-group (and its K/V tiles):
     // the largest of 8, 4, 2, 1 that divides both G and the wave count.
-    a.waves = a.window > 0 ? RBA_PREFILL_WAVES_LOCAL : RBA_PREFILL_WAVES_GLOBAL;
+    // The fused variant runs 8 waves on every layer.
+    a.waves = (a.window > 0 && !fused) ? RBA_PREFILL_WAVES_LOCAL : RBA_PREFILL_WAVES_GLOBAL;
     a.hpw = 1;
     while (a.hpw * 2 <= a.waves && a.G % (a.hpw * 2) == 0) a.hpw *= 2;
     const int qm = 32 * (a.waves / a.hpw);       // queries per head per work-group
@@ -176,7 +186,8 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
     // the kernel forms page offsets as (32-bit page id) x (32-bit page bytes)
     if ((long long)a.Hkv * a.page_size * kv->head_dim * 2 > 0xffffffffLL) return RBA_ERR_UNSUPPORTED;
     a.num_blocks = (int32_t)blocks;
-    err = rba::launch_prefill_bf16(a, kv->head_dim, stream);
+    err = fused ? rba::launch_prefill_fused(a, kv->head_dim, stream)
+                : rba::launch_prefill_bf16(a, kv->head_dim, stream);
   } else {
     a.num_qtiles = (max_seqlen + kF32Rows - 1) / kF32Rows;
     if (a.Hq > 65535 || a.num_seqs > 65535) return RBA_ERR_UNSUPPORTED;
@@ -184,6 +195,28 @@ RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int3
     err = rba::launch_prefill_f32(a, kv->head_dim, stream);
   }
   return err == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}
+
+}  // namespace
+
+RBA_EXPORT rba_status rba_prefill(const void *q, const int32_t *cu_seqlens, int32_t total_tokens,
+                                  int32_t max_seqlen, const rba_kv_cache *kv,
+                                  const rba_page_table *pt, const void *bias,
+                                  const rba_attn_params *params, void *out, float *lse,
+                                  hipStream_t stream) {
+  return prefill_impl(q, cu_seqlens, total_tokens, max_seqlen, kv, pt, bias, nullptr, nullptr, 0,
+                      params, out, lse, stream);
+}
+
+RBA_EXPORT rba_status rba_prefill_fused(const void *q, const int32_t *cu_seqlens,
+                                        int32_t total_tokens, int32_t max_seqlen,
+                                        const rba_kv_cache *kv, const rba_page_table *pt,
+                                        const void *rel_r, const void *w_rel_t, int32_t d_rel,
+                                        const rba_attn_params *params, void *out, float *lse,
+                                        hipStream_t stream) {
+  if (d_rel <= 0) return RBA_ERR_INVALID_ARG;
+  return prefill_impl(q, cu_seqlens, total_tokens, max_seqlen, kv, pt, nullptr, rel_r, w_rel_t,
+                      d_rel, params, out, lse, stream);
 }
 
 RBA_EXPORT rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu_new,

@@ -15,11 +15,14 @@ struct PrefillArgs {
   const void *v_pool;
   const int32_t *block_table; // [B][max_pages]
   const int32_t *seq_lens;    // prefill: keys held per sequence, this call's included (null: none before it)
-  const void *bias;          // [T][Hq][R]
+  const void *bias;          // [T][Hq][R] (null in the fused variant)
+  const void *rel_r;         // fused variant: [T][Hq][d_rel]
+  const void *w_rel_t;       // fused variant: [R][d_rel], W^T
   void *out;                 // [T][Hq][D]
   float *lse;                // [T][Hq] or null
   int32_t num_seqs, Hq, Hkv, G, max_pages, page_size, log2_page;
   int32_t window, R;
+  int32_t d_rel;             // fused variant: 16 or 32 (0 otherwise)
   int32_t total_tokens;      // T: rows of q, out and bias
   int32_t waves;             // waves per work-group (bf16 kernel: 4 or 8)
   int32_t hpw;               // query heads per work-group (divides G and waves)
@@ -62,6 +65,7 @@ struct AppendArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_prefill_fused(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStream_t s);

@@ -74,6 +74,27 @@ def oracle_prefill_history(case: ri.HistoryCase, rows=None, want_lse=False):
                                   sm_scale=sp.scale(), rows=rows, want_lse=want_lse)
 
 
+def gpu_prefill_fused(case: ri.ProjectedCase, want_lse=False, seq_lens="case"):
+    h = case.hist
+    sp = h.spec
+    lse = None
+    if want_lse:
+        lse = torch.empty((h.total_tokens, sp.num_q_heads), dtype=torch.float32,
+                          device=h.q.device)
+    out = rba.prefill_fused(h.q, h.cu_seqlens, h.max_seqlen, h.k_pool, h.v_pool, h.block_table,
+                            h.seq_lens_dev if seq_lens == "case" else seq_lens, case.rel_r,
+                            case.w_rel_t, window=sp.window, sm_scale=sp.scale(), lse=lse)
+    return (out, lse) if want_lse else out
+
+
+def oracle_prefill_projected(case: ri.ProjectedCase, rows=None, want_lse=False):
+    h = case.hist
+    sp = h.spec
+    return oracle.prefill_projected(h.q, h.k_log, h.v_log, case.rel_r, case.w_rel, h.cu_list(),
+                                    h.cu_kv_list(), window=sp.window, sm_scale=sp.scale(),
+                                    rows=rows, want_lse=want_lse)
+
+
 def gpu_decode(case: ri.DecodeCase, num_splits=0, want_lse=False, block_table=None,
                k_pool=None, v_pool=None, max_seq_len=None):
     sp = case.spec

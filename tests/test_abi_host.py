@@ -53,6 +53,12 @@ def _prefill(kv, pt, prm, q=FAKE, cu=FAKE, T=100, max_len=50, bias=FAKE, out=FAK
                                   ctypes.byref(prm), out, lse, None)
 
 
+def _prefill_fused(kv, pt, prm, q=FAKE, cu=FAKE, T=100, max_len=50, r=FAKE, w=FAKE, d_rel=32,
+                   out=FAKE, lse=None):
+    return rba.load().rba_prefill_fused(q, cu, T, max_len, ctypes.byref(kv), ctypes.byref(pt), r,
+                                        w, d_rel, ctypes.byref(prm), out, lse, None)
+
+
 def _decode(kv, pt, prm, q=FAKE, max_len=1000, bias=FAKE, splits=0, ws=None, ws_bytes=0,
             out=FAKE, lse=None):
     return rba.load().rba_decode(q, ctypes.byref(kv), ctypes.byref(pt), max_len, bias,
@@ -103,6 +109,43 @@ def test_prefill_empty_is_noop():
     assert _prefill(kv, pt, prm, q=0, cu=0, bias=0, out=0, T=0) == rba.RBA_OK
     kv, pt, prm = _layer(seqs=0)
     assert _prefill(kv, pt, prm, q=0, cu=0, bias=0, out=0) == rba.RBA_OK
+
+
+@pytest.mark.parametrize("kwargs,expected", [
+    (dict(q=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(cu=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(r=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(w=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(out=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(r=FAKE + 8), rba.RBA_ERR_INVALID_ARG),
+    (dict(w=FAKE + 2), rba.RBA_ERR_INVALID_ARG),
+    (dict(d_rel=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(d_rel=-16), rba.RBA_ERR_INVALID_ARG),
+    (dict(d_rel=64), rba.RBA_ERR_UNSUPPORTED),
+    (dict(d_rel=24), rba.RBA_ERR_UNSUPPORTED),
+    (dict(T=-1), rba.RBA_ERR_INVALID_ARG),
+    (dict(max_len=256 * 64 + 1), rba.RBA_ERR_INVALID_ARG),
+])
+def test_prefill_fused_argument_errors(kwargs, expected):
+    kv, pt, prm = _layer()
+    assert _prefill_fused(kv, pt, prm, **kwargs) == expected
+
+
+def test_prefill_fused_needs_bf16_pools():
+    kv, pt, prm = _layer(dtype=rba.RBA_F32)
+    assert _prefill_fused(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED
+
+
+def test_prefill_fused_shares_the_layer_checks():
+    kv, pt, prm = _layer(hq=30, hkv=8)
+    assert _prefill_fused(kv, pt, prm) == rba.RBA_ERR_INVALID_ARG
+    kv, pt, prm = _layer(d=96)
+    assert _prefill_fused(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED
+
+
+def test_prefill_fused_empty_is_noop():
+    kv, pt, prm = _layer()
+    assert _prefill_fused(kv, pt, prm, T=0, q=0, r=0, w=0, out=0) == rba.RBA_OK
 
 
 @pytest.mark.parametrize("kwargs", [
