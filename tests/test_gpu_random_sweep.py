@@ -2,8 +2,9 @@
 oracle: query/KV head counts with GQA 1..8, head_dim 64/128, windows shorter
 and longer than the bias extent (and full causal), extents from 1 to beyond
 the sequence, page sizes 16..256, ragged and empty sequences, histories, and
-forced decode partition counts.  Sizes stay small enough for the oracle to
-check every row.
+forced decode partition counts, and the prefill with the bias formed in the
+kernel (d_rel 16 or 32).  Sizes stay small enough for the oracle to check
+every row.
 """
 import random
 import zlib
@@ -14,7 +15,8 @@ import torch
 
 import rba_inputs as ri
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, gpu_decode, gpu_prefill,
-                         oracle_decode, oracle_prefill, oracle_prefill_history)
+                         gpu_prefill_fused, oracle_decode, oracle_prefill, oracle_prefill_history,
+                         oracle_prefill_projected)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +102,25 @@ def test_random_fp32(i, seed):
     torch.cuda.synchronize()
     assert_parity(out, oracle_prefill(pre), torch.float32, f"fp32 prefill #{i} {sp}")
     assert_parity(dout, oracle_decode(dec), torch.float32, f"fp32 decode #{i} {sp}")
+
+
+@pytest.mark.parametrize("i,seed", _cases("fused", 12))
+def test_random_prefill_fused(i, seed):
+    rng = random.Random(seed)
+    sp = _random_spec(rng)
+    B = rng.randint(1, 4)
+    keys = [rng.choice([0, 1, 5, 64, 65, 130, 400, 1000]) for _ in range(B)]
+    if sum(keys) == 0:
+        keys[0] = 7
+    new = None
+    if rng.random() < 0.5:
+        new = [rng.randint(1, k) if k > 0 and rng.random() < 0.7 else k for k in keys]
+    d_rel = rng.choice([16, 32])
+    case = ri.make_projected(sp, keys, new, d_rel, seed=seed % 100000, device=device())
+    out, lse = gpu_prefill_fused(case, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_prefill_projected(case, want_lse=True)
+    what = f"fused #{i} {sp} keys={keys} new={new} d_rel={d_rel}"
+    assert_parity(out, ref, sp.dtype, what)
+    if ref_lse.size:
+        assert np.max(np.abs(lse.cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS, what
