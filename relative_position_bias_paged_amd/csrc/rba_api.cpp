@@ -25,7 +25,7 @@ namespace {
 #endif
 constexpr int kF32Rows = 64;         // queries per fp32 prefill work-group
 constexpr int kMaxSplits = 256;
-constexpr int kAutoChunkPages = 32;  // automatic partitions hold about this many pages
+constexpr int kAutoChunkPages = 64;  // automatic partitions hold about this many pages
 constexpr long long kAutoMinWaves = 2048;
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
