@@ -436,7 +436,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   auto fuse_bias = [&](const uint16_t *wsl) {
     if constexpr (FUSED) {
       const uint16_t *wa = wsl + (32 * qb + col) * DR + half * 8;
-      uint16_t *sb = stage_w + 32 + (FUSED_ROW - 1) * col + 4 * half;
+      // 2-byte stores, kept apart: merged into 8-byte ones they would sit at
+      // 2-byte-aligned addresses, which LDS serves with long stalls
+      typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+      volatile lds_u16_t *sb = (volatile lds_u16_t *)(stage_w + 32 + (FUSED_ROW - 1) * col + 4 * half);
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         f32x16_t acc;
