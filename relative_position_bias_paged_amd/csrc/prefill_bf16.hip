@@ -126,13 +126,21 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
 // 11:8) that waits for LDS and scalar memory traffic only.
 constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
 
-// Fused stage layout: row q of a wave's stage starts at element 32 + 96*q and
-// holds distance index e (0..63 in use) at +e.  The product for distance
-// index idx = e + q of query q is written at 32 + 95*q + idx, so a lane's
+// Fused stage layout: row q of a wave's stage starts at element 32 + 104*q
+// and holds distance index e (0..63 in use) at +e.  The product for distance
+// index idx = e + q of query q is written at 32 + 103*q + idx, so a lane's
 // writes sit at fixed offsets from one per-lane base; the indices it also
-// computes outside 0..63 (-31..95) land in the unused elements 64..95 of its
-// own or the previous row, or in the 32-element head.
-constexpr int FUSED_ROW = 96;
+// computes outside 0..63 (-31..95) land in the unused elements 64..103 of its
+// own or the previous row, or in the 32-element head.  Rows 208 bytes apart
+// put the 16 rows one aligned 16-byte read serves on distinct banks.
+constexpr int FUSED_ROW = 104;
+// chunk swizzle of W^T row r in the fused variant's LDS buffers: rows are
+// 2*DR bytes, 128/DR of them fill the 64 banks, so the swizzle steps once
+// per that many rows
+template <int DR>
+__device__ __forceinline__ int wsl_swizzle(int r) {
+  return (r / (128 / DR)) % (DR / 8);
+}
 constexpr int FUSED_STAGE = 32 + 32 * FUSED_ROW;
 
 template <int D, int NW, bool BIG_PAGE, bool VEC_BIAS, int DR>
@@ -155,7 +163,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   __shared__ __align__(16) uint16_t bias_stage[NW * STAGE_W];
   // fused variant: two buffers of W^T rows (distances P0-s0-63 .. P0+QM-1-s0
   // of tile s0, P0 the work-group's first query position), at most 32*NW+64
-  // rows of DR elements
+  // rows of DR elements; the 16-byte chunks of row r are XOR-swizzled by
+  // wsl_swizzle(r) so that 16 consecutive rows read on distinct banks
   constexpr int WSL_ROWS = 32 * NW + 64;
   uint16_t *wsl0 = nullptr, *wsl1 = nullptr;
   if constexpr (FUSED) {
@@ -423,8 +432,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const int n_ld = (QM + 64) / RPI;
       const int d0 = P0 - s0 - (BN - 1);
       for (int i = wave; i < n_ld; i += NW) {
-        const int dd = min(max(d0 + i * RPI + lane / LPR, 0), R - 1);
-        dma16(wt + (size_t)dd * DR + (lane % LPR) * 8, (lds_void_t *)(dst + i * 512));
+        const int rr = i * RPI + lane / LPR;                 // buffer row this lane fills
+        const int dd = min(max(d0 + rr, 0), R - 1);
+        const int c = (lane % LPR) ^ wsl_swizzle<DR>(rr);    // logical chunk it fetches
+        dma16(wt + (size_t)dd * DR + c * 8, (lds_void_t *)(dst + i * 512));
       }
     }
   };
@@ -435,7 +446,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // 32 + 95*col + idx of the stage.
   auto fuse_bias = [&](const uint16_t *wsl) {
     if constexpr (FUSED) {
-      const uint16_t *wa = wsl + (32 * qb + col) * DR + half * 8;
+      // row 32*qb + 32*b + col, logical chunk 2*kk + half (the swizzle of a
+      // row depends on col only: 32 rows are whole swizzle periods)
+      const int wsw = wsl_swizzle<DR>(col);
+      const uint16_t *wa = wsl + (32 * qb + col) * DR;
       // 2-byte stores, kept apart: merged into 8-byte ones they would sit at
       // 2-byte-aligned addresses, which LDS serves with long stalls
       typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
@@ -447,7 +461,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < DR / 16; ++kk) {
-          const u32x4_t w = *reinterpret_cast<const u32x4_t *>(wa + 32 * b * DR + kk * 16);
+          const u32x4_t w = *reinterpret_cast<const u32x4_t *>(wa + 32 * b * DR + ((2 * kk + half) ^ wsw) * 8);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w),
                                                         __builtin_bit_cast(bf16x8_t, rf[kk]), acc, 0, 0, 0);
         }
