@@ -443,7 +443,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // over 96 distance indices in three 32-row MFMA blocks (A = W^T rows from
   // the buffer, B = r), rounded to bf16.  Register 4i+j of block b holds
   // index idx = 32b + 8i + 4*half + j of query col, written at
-  // 32 + 95*col + idx of the stage.
+  // 32 + 103*col + idx of the stage.
   auto fuse_bias = [&](const uint16_t *wsl) {
     if constexpr (FUSED) {
       // row 32*qb + 32*b + col, logical chunk 2*kk + half (the swizzle of a
