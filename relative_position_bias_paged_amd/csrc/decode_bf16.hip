@@ -148,7 +148,9 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   // Every load is unconditional: a tile index past the end re-reads the last
   // tile (already in cache), heads past nh read a valid row, and clamp-only
   // tiles read bucket R-1, so no load sits behind a branch and the waits
-  // before each tile's use only cover that tile.
+  // before each tile's use only cover that tile.  K and V are read once, by
+  // this wave only, so they are loaded with the streaming (non-temporal)
+  // cache policy, which sustains a higher HBM read rate than the default one.
   auto issue = [&](int ti, TileBuf<D> &tb) {
     const int ts = k_lo + min(ti, ntiles - 1) * 16;     // first key of the tile
     const int page = trow[ts >> lp];
@@ -156,15 +158,16 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
                         (size_t)(ts & (P - 1)) * D;
     const uint16_t *kt = kp + base + (size_t)c16 * D + 8 * g4;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) tb.k[kk] = *reinterpret_cast<const u32x4_t *>(kt + 32 * kk);
+    for (int kk = 0; kk < KK; ++kk)
+      tb.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kt + 32 * kk));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint16_t *vt = vp + base + (size_t)(4 * g4 + i) * D + DV * c16;
       if constexpr (KK == 4) {
-        const u32x4_t w = *reinterpret_cast<const u32x4_t *>(vt);
+        const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vt));
         tb.v[i][0] = w[0]; tb.v[i][1] = w[1]; tb.v[i][2] = w[2]; tb.v[i][3] = w[3];
       } else {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(vt);
+        const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(vt));
         tb.v[i][0] = w[0]; tb.v[i][1] = w[1];
       }
     }
