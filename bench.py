@@ -320,8 +320,10 @@ def secondary(name, torch, rba, ri, steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU takes some 10-20 ms of back-to-back work to reach its steady
+    # clocks; the default warm-up covers that (about 15 ms on the headline)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=MAIN)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -444,7 +446,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_secondary:
         result["secondary"] = [secondary(n, torch, rba, ri, steps=max(5, args.steps // 5),
-                                         warmup=2) for n in SECONDARY if n != args.workload]
+                                         warmup=max(2, args.warmup // 5))
+                               for n in SECONDARY if n != args.workload]
     print(json.dumps(result), flush=True)
 
 
