@@ -198,7 +198,10 @@ size_t rba_decode_workspace_size(const rba_kv_cache *kv,
  * more than one partition the visible key range of each sequence is cut into
  * page-aligned partitions, each partition's normalised partial output and
  * log-sum-exp go to the workspace, and a second kernel merges them with
- * weights exp(lse_j - max_j lse_j).
+ * weights exp(lse_j - max_j lse_j).  A one-work-group kernel launched first
+ * orders the (sequence, partition) pairs largest first from seq_lens on the
+ * device, into the workspace, so that the grid hands out the longest
+ * partitions first; the order changes no result.
  *
  *  q           [num_seqs][Hq][head_dim]
  *  max_seq_len host bound on max_b seq_lens[b] (sizes the grid)

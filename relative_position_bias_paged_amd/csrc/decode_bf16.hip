@@ -26,6 +26,15 @@
 //    at the end.
 // Partitions write a normalised fp32 partial output and its natural-log LSE
 // to the workspace; merge_kernel combines them with weights exp(lse_j - max).
+//
+// With partitions, plan_kernel first orders the (sequence, partition) items
+// largest first (a counting sort on the device, so the host never reads the
+// sequence lengths).  The hardware hands out work-groups in grid order, and
+// one wave streams at most a few GB/s however idle the memory system is, so
+// a long partition dispatched late would run on alone at the end; largest
+// first leaves the short ones for the tail.  The order changes no result:
+// every partition writes its own slot and the merge reads them in a fixed
+// order.
 #include "rba_internal.h"
 
 namespace rba {
@@ -94,8 +103,19 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   item /= HG;
   const int kvh = item % a.Hkv;
   item /= a.Hkv;
-  const int b = item % a.num_seqs;
-  const int split = item / a.num_seqs;
+  int b, split, n;
+  if (a.plan != nullptr) {
+    // item-th largest (sequence, partition); the record carries the length
+    const int2 rec = a.plan[item];
+    if (rec.x < 0) return;               // a partition with no key: nothing to merge
+    b = rec.x / S;
+    split = rec.x - b * S;
+    n = rec.y;
+  } else {
+    b = item % a.num_seqs;
+    split = item / a.num_seqs;
+    n = a.seq_lens[b];
+  }
 
   const int G = a.G;
   const int h_base = kvh * G + hg * 4;
@@ -106,7 +126,6 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   const int P = a.page_size;
   const int lp = a.log2_page;
 
-  const int n = a.seq_lens[b];
   const int t = n - 1;
   const int lo = (W > 0) ? max(0, n - W) : 0;
   const int p_first = lo >> lp;
@@ -116,6 +135,8 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   const int k_lo = max(pg_lo << lp, lo) & ~15;         // first 16-key tile
   const int k_hi = min(pg_hi << lp, n);                // exclusive
   const int ntiles = (n > 0 && pg_lo < pg_hi) ? (k_hi - k_lo + 15) >> 4 : 0;
+  // the merge reads only partitions that hold keys
+  if (S > 1 && ntiles == 0) return;
 
   const uint16_t *qp = static_cast<const uint16_t *>(a.q);
   const uint16_t *kp = static_cast<const uint16_t *>(a.k_pool);
@@ -314,22 +335,27 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
 }
 
 // One wave per (sequence, query head): out = sum_j w_j o_j / sum_j w_j with
-// w_j = exp(lse_j - max_j lse_j); partitions with lse = -inf carry no weight.
+// w_j = exp(lse_j - max_j lse_j) over the partitions that hold keys (the
+// first ceil((p_end - p_first) / chunk) of them; the others wrote nothing).
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int bf16_out) {
   constexpr int E = D / 64;      // elements per lane
   const int lane = threadIdx.x;
   const size_t orow = blockIdx.x;
   const int S = a.num_splits;
+  const int n = a.seq_lens[orow / a.Hq];
+  const int lo = (a.window > 0) ? max(0, n - a.window) : 0;
+  const int span = ((n + a.page_size - 1) >> a.log2_page) - (lo >> a.log2_page);
+  const int S_b = n > 0 ? min(S, (span + a.chunk_pages - 1) / a.chunk_pages) : 0;
   const float *pl = a.part_lse + orow * S;
   float M = -INFINITY;
-  for (int j = 0; j < S; ++j) M = fmaxf(M, pl[j]);
+  for (int j = 0; j < S_b; ++j) M = fmaxf(M, pl[j]);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (M > -INFINITY) {
-    for (int j = 0; j < S; ++j) {
+    for (int j = 0; j < S_b; ++j) {
       const float lj = pl[j];
       if (lj > -INFINITY) {
         const float w = __expf(lj - M);
@@ -353,7 +379,57 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int bf16_out) {
   if (a.lse != nullptr && lane == 0) a.lse[orow] = (wsum > 0.f) ? M + __logf(wsum) : -INFINITY;
 }
 
+// Largest-first order of the (sequence, partition) items for the decode grid:
+// a counting sort on (chunk_pages - pages) >> plan_shift, with the empty
+// partitions last as {-1, 0}.  One work-group; positions within a bucket
+// follow LDS atomics, which changes dispatch order only, never a result.
+constexpr int kPlanBuckets = 257;        // 256 size classes + the empty ones
+__global__ __launch_bounds__(1024) void plan_kernel(DecodeArgs a) {
+  __shared__ int hist[kPlanBuckets];
+  const int S = a.num_splits;
+  const int C = a.chunk_pages;
+  const int items = a.num_seqs * S;
+  const int lp = a.log2_page;
+  auto bucket_of = [&](int it, int &n) {
+    const int b = it / S;
+    const int j = it - b * S;
+    n = a.seq_lens[b];
+    const int lo = (a.window > 0) ? max(0, n - a.window) : 0;
+    const int p_first = lo >> lp;
+    const int p_end = (n + a.page_size - 1) >> lp;
+    const int pages = (n > 0) ? max(0, min(p_first + (j + 1) * C, p_end) - (p_first + j * C)) : 0;
+    return pages > 0 ? (C - pages) >> a.plan_shift : kPlanBuckets - 1;
+  };
+  for (int i = threadIdx.x; i < kPlanBuckets; i += blockDim.x) hist[i] = 0;
+  __syncthreads();
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    int n;
+    atomicAdd(&hist[bucket_of(it, n)], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {                // exclusive prefix over the buckets
+    int run = 0;
+    for (int k = 0; k < kPlanBuckets; ++k) {
+      const int c = hist[k];
+      hist[k] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < items; it += blockDim.x) {
+    int n;
+    const int k = bucket_of(it, n);
+    const int pos = atomicAdd(&hist[k], 1);
+    a.plan[pos] = (k == kPlanBuckets - 1) ? int2{-1, 0} : int2{it, n};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s) {
   const long long items = (long long)a.num_seqs * a.Hkv * a.num_splits * a.head_groups;

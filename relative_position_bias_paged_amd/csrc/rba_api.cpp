@@ -101,13 +101,27 @@ SplitPlan plan_splits(const rba_kv_cache *kv, const rba_page_table *pt, int max_
   return {s, chunk};
 }
 
+// Decode workspace with S > 1 partitions, each part starting 256-byte aligned:
+// partial outputs fp32 [B][Hq][S][D], their LSE fp32 [B][Hq][S], and the
+// largest-first plan of the B*S (sequence, partition) items, two int32 each.
+struct WorkspaceLayout {
+  size_t lse_off, plan_off, bytes;
+};
+
+size_t pad256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WorkspaceLayout workspace_layout(const rba_kv_cache *kv, const rba_page_table *pt,
+                                 const rba_attn_params *p, int splits) {
+  if (splits <= 1) return {0, 0, 0};
+  const size_t rows = (size_t)pt->num_seqs * p->num_q_heads;
+  const size_t lse_off = pad256(rows * splits * kv->head_dim * sizeof(float));
+  const size_t plan_off = pad256(lse_off + rows * splits * sizeof(float));
+  return {lse_off, plan_off, plan_off + (size_t)pt->num_seqs * splits * 2 * sizeof(int32_t)};
+}
+
 size_t workspace_bytes_for(const rba_kv_cache *kv, const rba_page_table *pt,
                            const rba_attn_params *p, int splits) {
-  if (splits <= 1) return 0;
-  const size_t rows = (size_t)pt->num_seqs * p->num_q_heads;
-  const size_t o_bytes = rows * splits * kv->head_dim * sizeof(float);
-  const size_t o_padded = (o_bytes + 255) & ~(size_t)255;
-  return o_padded + rows * splits * sizeof(float);
+  return workspace_layout(kv, pt, p, splits).bytes;
 }
 
 }  // namespace
@@ -323,11 +337,15 @@ RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rb
   a.chunk_pages = sp.chunk_pages;
   a.head_groups = (a.G + 3) / 4;
   if (need > 0) {
-    const size_t rows = (size_t)a.num_seqs * a.Hq;
-    const size_t o_bytes = rows * sp.splits * kv->head_dim * sizeof(float);
-    a.part_o = static_cast<float *>(workspace);
-    a.part_lse = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                           ((o_bytes + 255) & ~(size_t)255));
+    const WorkspaceLayout wl = workspace_layout(kv, pt, params, sp.splits);
+    char *base = static_cast<char *>(workspace);
+    a.part_o = reinterpret_cast<float *>(base);
+    a.part_lse = reinterpret_cast<float *>(base + wl.lse_off);
+    if (kv->dtype == RBA_BF16) {
+      a.plan = reinterpret_cast<int2 *>(base + wl.plan_off);
+      a.plan_shift = 0;
+      while (((sp.chunk_pages - 1) >> a.plan_shift) > 255) ++a.plan_shift;
+    }
   }
 
   hipError_t err;
@@ -336,6 +354,11 @@ RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rb
   } else {
     const long long items = (long long)a.num_seqs * a.Hkv * a.num_splits * a.head_groups;
     if (items > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
+    if (a.plan != nullptr) {
+      if ((long long)a.num_seqs * a.num_splits > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
+      err = rba::launch_decode_plan(a, stream);
+      if (err != hipSuccess) return RBA_ERR_HIP;
+    }
     err = rba::launch_decode_bf16(a, kv->head_dim, stream);
     if (err == hipSuccess && sp.splits > 1) err = rba::launch_merge(a, kv->head_dim, true, stream);
   }

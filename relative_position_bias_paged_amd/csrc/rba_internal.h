@@ -43,6 +43,11 @@ struct DecodeArgs {
   float *lse;                // [B][Hq] or null
   float *part_o;             // [B][Hq][S][D] when S > 1
   float *part_lse;           // [B][Hq][S]   when S > 1
+  // When S > 1: the (sequence, partition) items largest first, as written by
+  // the plan kernel: {b * S + partition, seq_lens[b]}, then {-1, 0} for the
+  // partitions that hold no key.  Null: the grid order is used as it is.
+  int2 *plan;
+  int32_t plan_shift;        // plan buckets: (chunk_pages - pages) >> plan_shift
   int32_t num_seqs, Hq, Hkv, G, max_pages, page_size, log2_page;
   int32_t window, R;
   int32_t num_splits;        // S
@@ -69,6 +74,7 @@ hipError_t launch_prefill_fused(const PrefillArgs &a, int head_dim, hipStream_t 
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStream_t s);
+hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, int head_dim, hipStream_t s);
 

@@ -190,7 +190,9 @@ def test_decode_split_plan():
     n, ws = plan(131072, 16, seqs=32, max_pages=2048, pages=65536)
     assert n == 16
     rows = 32 * 32
-    assert ws == rows * 16 * 128 * 4 + rows * 16 * 4
+    # partial outputs and LSE, each 256-byte aligned, then the largest-first
+    # plan: two int32 per (sequence, partition)
+    assert ws == rows * 16 * 128 * 4 + rows * 16 * 4 + 32 * 16 * 8
     # one partition: no workspace
     assert plan(4096, 1, seqs=4)[1] == 0
     # never more partitions than pages

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import rba_inputs as ri
+import relative_position_bias_paged_amd as rba
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, errors, gpu_decode,
                          gpu_prefill, oracle_decode)
 
@@ -75,6 +76,36 @@ def test_empty_sequence_gives_zero_row():
         assert torch.all(torch.isneginf(lse[1]))
         ref = oracle_decode(case, seqs=[0])
         assert_parity(out[:1], ref, torch.bfloat16, "row 0")
+
+
+def test_workspace_contents_are_ignored():
+    """Ragged lengths under 16 partitions: most sequences fill only some of
+    them, and one is empty.  Partitions that hold no key write nothing, and
+    the merge must not read their slots, so a workspace filled with NaN
+    (0xFF bytes) beforehand must not change the result."""
+    dev = device()
+    sp = spec(32, 8, 128, 0, 1024, 64)
+    lens = [9000, 1, 64, 65, 3000, 4097, 130, 2049, 17, 8191]
+    case = ri.make_decode(sp, lens, seed=33, device=dev)
+    empty = 4
+    lens_dev = case.seq_lens_dev.clone()
+    lens_dev[empty] = 0
+    case0 = ri.DecodeCase(**{**case.__dict__, "seq_lens_dev": lens_dev})
+    need = rba.decode_workspace_size(case.q, case.k_pool, case.v_pool, case.block_table,
+                                     lens_dev, case.max_seq_len, case.bias, window=0,
+                                     sm_scale=sp.scale(), num_splits=16)
+    for fill in (0xFF, 0x00):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=dev)
+        lse = torch.empty(case.q.shape[:2], dtype=torch.float32, device=dev)
+        out = rba.decode(case.q, case.k_pool, case.v_pool, case.block_table, lens_dev,
+                         case.max_seq_len, case.bias, window=0, sm_scale=sp.scale(),
+                         num_splits=16, workspace=ws, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+        keep = [b for b in range(len(lens)) if b != empty]
+        ref, ref_lse = oracle_decode(case0, seqs=keep, want_lse=True)
+        assert_parity(out[keep], ref, sp.dtype, f"ragged, workspace filled with {fill:#x}")
+        assert np.max(np.abs(lse[keep].cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS
 
 
 def test_split_counts_agree():
