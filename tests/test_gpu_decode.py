@@ -108,6 +108,20 @@ def test_workspace_contents_are_ignored():
         assert np.max(np.abs(lse[keep].cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS
 
 
+def test_long_partitions_plan():
+    """Two partitions of 313 pages: the largest-first plan groups partition
+    sizes into 256 classes by a shift, and a short sequence's partitions sit
+    in other classes than the long one's."""
+    dev = device()
+    sp = spec(8, 2, 128, 0, 1024, 64)
+    case = ri.make_decode(sp, [40000, 300, 20001], seed=41, device=dev)
+    out, lse = gpu_decode(case, num_splits=2, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode(case, want_lse=True)
+    assert_parity(out, ref, sp.dtype, "two long partitions")
+    assert np.max(np.abs(lse.cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS
+
+
 def test_split_counts_agree():
     dev = device()
     sp = spec(32, 8, 128, 0, 1024, 64)
