@@ -118,10 +118,14 @@ def decode_work(case):
 
 
 def source_hash(*names):
+    """Hash of kernel sources together with their compile flags: counters
+    taken on another build of the same source do not describe this one."""
+    from relative_position_bias_paged_amd import build as hip_build
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "relative_position_bias_paged_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+        h.update(" ".join(hip_build.EXTRA_FLAGS.get(n, [])).encode())
     return h.hexdigest()
 
 

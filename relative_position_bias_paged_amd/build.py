@@ -20,8 +20,11 @@ LIB = os.path.join(HERE, "librba.so")
 
 SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "kv_append.hip", "rba_api.cpp"]
 # The bf16 attention kernels never test for NaN (masking selects, it does not
-# multiply), so fmax needs no NaN-quieting of its operands.
-EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+# multiply), so fmax needs no NaN-quieting of its operands.  The prefill
+# kernels are scheduled with LLVM's iterative ILP strategy: it interleaves
+# their matrix and vector work better than the default (global-layer prefill
+# ~3% faster, windowed layers within 1-2% either way).
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 ARCH = os.environ.get("RBA_OFFLOAD_ARCH", "gfx950")
 
 
