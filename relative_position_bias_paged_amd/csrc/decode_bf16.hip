@@ -169,9 +169,12 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
   // Every load is unconditional: a tile index past the end re-reads the last
   // tile (already in cache), heads past nh read a valid row, and clamp-only
   // tiles read bucket R-1, so no load sits behind a branch and the waits
-  // before each tile's use only cover that tile.  K and V are read once, by
-  // this wave only, so they are loaded with the streaming (non-temporal)
-  // cache policy, which sustains a higher HBM read rate than the default one.
+  // before each tile's use only cover that tile.  V is read once, by this
+  // wave only, each load instruction covering whole 128-byte lines, so it is
+  // loaded with the streaming (non-temporal) cache policy, which sustains a
+  // higher HBM read rate.  K keeps the default policy: its two load
+  // instructions per 32 head-dim elements each read half of the same lines,
+  // and under the streaming policy the second half was often fetched again.
   auto issue = [&](int ti, TileBuf<D> &tb) {
     const int ts = k_lo + min(ti, ntiles - 1) * 16;     // first key of the tile
     const int page = trow[ts >> lp];
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
     const uint16_t *kt = kp + base + (size_t)c16 * D + 8 * g4;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      tb.k[kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kt + 32 * kk));
+      tb.k[kk] = *reinterpret_cast<const u32x4_t *>(kt + 32 * kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint16_t *vt = vp + base + (size_t)(4 * g4 + i) * D + DV * c16;
