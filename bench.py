@@ -145,12 +145,19 @@ def recorded_traffic(workload: str, kernel_source: str):
 # ---------------------------------------------------------------------------
 # timing
 
-def time_steps(step, steps: int, warmup: int, torch):
-    """Run warmup, then `steps` timed steps.  Returns (wall ms per step,
-    mean event ms per launch of the timed steps)."""
+def time_steps(step, steps: int, warmup: int, torch, min_warm_ms: float = 0.0):
+    """Run warmup (at least `warmup` steps, and at least `min_warm_ms` of
+    back-to-back work), then `steps` timed steps.  Returns (wall ms per
+    step, mean event ms per launch of the timed steps)."""
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        while (time.perf_counter() - t0) * 1e3 < min_warm_ms:
+            for _ in range(max(1, warmup)):
+                step()
+            torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -211,7 +218,7 @@ def cpu_baseline(case, budget_s: float):
 
 # ---------------------------------------------------------------------------
 
-def run_prefill(case, steps, warmup, torch, rba):
+def run_prefill(case, steps, warmup, torch, rba, min_warm_ms=0.0):
     sp = case.spec
     out = torch.empty_like(case.q)
 
@@ -220,10 +227,10 @@ def run_prefill(case, steps, warmup, torch, rba):
                     case.block_table, case.seq_lens_dev, case.bias, window=sp.window,
                     sm_scale=sp.scale(), out=out)
 
-    return time_steps(step, steps, warmup, torch)
+    return time_steps(step, steps, warmup, torch, min_warm_ms)
 
 
-def run_prefill_fused(case, steps, warmup, torch, rba):
+def run_prefill_fused(case, steps, warmup, torch, rba, min_warm_ms=0.0):
     h = case.hist
     sp = h.spec
     out = torch.empty_like(h.q)
@@ -233,10 +240,10 @@ def run_prefill_fused(case, steps, warmup, torch, rba):
                           h.seq_lens_dev, case.rel_r, case.w_rel_t, window=sp.window,
                           sm_scale=sp.scale(), out=out)
 
-    return time_steps(step, steps, warmup, torch)
+    return time_steps(step, steps, warmup, torch, min_warm_ms)
 
 
-def run_decode(cases, splits, steps, warmup, torch, rba):
+def run_decode(cases, splits, steps, warmup, torch, rba, min_warm_ms=0.0):
     ws = {}
     outs = {}
     for key, c in cases.items():
@@ -254,10 +261,10 @@ def run_decode(cases, splits, steps, warmup, torch, rba):
                        c.bias, window=sp.window, sm_scale=sp.scale(), num_splits=splits,
                        workspace=ws[key], out=outs[key])
 
-    return time_steps(step, steps, warmup, torch)
+    return time_steps(step, steps, warmup, torch, min_warm_ms)
 
 
-def secondary(name, torch, rba, ri, steps, warmup):
+def secondary(name, torch, rba, ri, steps, warmup, min_warm_ms=0.0):
     w = ri.WORKLOADS[name]
     cases = ri.build_workload(name, torch.device("cuda:0"))
     if w["kind"] == "append":
@@ -269,7 +276,7 @@ def secondary(name, torch, rba, ri, steps, warmup):
             rba.kv_append(c.k_new, c.v_new, c.cu_new, c.k_pool, c.v_pool, c.block_table,
                           c.seq_lens_dev)
 
-        wall, ev = time_steps(step, steps, warmup, torch)
+        wall, ev = time_steps(step, steps, warmup, torch, min_warm_ms)
         gbs = byt / (ev * 1e-3) / 1e9
         return {"workload": name, "metric": "K/V append GB/s", "value": round(gbs, 1),
                 "unit": "GB/s", "ms_per_step": round(wall, 4), "kernel_ms": round(ev, 4),
@@ -282,9 +289,9 @@ def secondary(name, torch, rba, ri, steps, warmup):
                 "prefill-projected": prefill_projected_work}[w["kind"]]
         flops, byt = work(case)
         if w["kind"] == "prefill-projected":
-            wall, ev = run_prefill_fused(case, steps, warmup, torch, rba)
+            wall, ev = run_prefill_fused(case, steps, warmup, torch, rba, min_warm_ms)
         else:
-            wall, ev = run_prefill(case, steps, warmup, torch, rba)
+            wall, ev = run_prefill(case, steps, warmup, torch, rba, min_warm_ms)
         tf = flops / (ev * 1e-3) / 1e12
         gbs = byt / (ev * 1e-3) / 1e9
         if w["kind"] != "prefill" and flops / byt < RIDGE_FLOP_PER_BYTE:
@@ -304,7 +311,7 @@ def secondary(name, torch, rba, ri, steps, warmup):
             f, b = decode_work(c)
             flops += f
             byt += b
-        wall, ev = run_decode(cases, splits, steps, warmup, torch, rba)
+        wall, ev = run_decode(cases, splits, steps, warmup, torch, rba, min_warm_ms)
         gbs = byt / (ev * 1e-3) / 1e9
         res = {"workload": name, "metric": "decode KV-read GB/s", "value": round(gbs, 1),
                "unit": "GB/s", "ms_per_step": round(wall, 4), "step_event_ms": round(ev, 4),
@@ -449,8 +456,10 @@ def main():
     del case
     torch.cuda.empty_cache()
     if not args.no_secondary:
+        # after the oracle's pause the clocks have dropped again: each short
+        # secondary warms for a fixed stretch of work, not just a step count
         result["secondary"] = [secondary(n, torch, rba, ri, steps=max(5, args.steps // 5),
-                                         warmup=max(2, args.warmup // 5))
+                                         warmup=max(2, args.warmup // 5), min_warm_ms=30.0)
                                for n in SECONDARY if n != args.workload]
     print(json.dumps(result), flush=True)
 
