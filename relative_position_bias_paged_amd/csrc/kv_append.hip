@@ -6,9 +6,15 @@
 // page, the commit that borrows the framework page table: positional
 // entries, bounded by the sequence length).
 //
-// One thread per 16-byte chunk of a new (token, KV head) row, so a row is
-// written by consecutive lanes.  A position outside the table or a page id
-// outside the pool is a broken caller contract: that chunk is not written.
+// One thread per 16-byte chunk of a new token's row, for a group of two KV
+// heads: the sequence lookup and the page read serve both rows, and all four
+// loads (K and V of both heads) are in flight before the first store.  The
+// lanes of a chunk run cover consecutive tokens, so a page's slots are written
+// by consecutive lanes.  The new rows are read once, with streaming loads.
+// Larger head groups were measured slower: more rows per thread puts more
+// writes of one wave 16 KB apart, at the same position in different pages.
+// A position outside the table or a page id outside the pool is a broken
+// caller contract: that token's rows are not written.
 #include "rba_internal.h"
 
 namespace rba {
@@ -16,14 +22,14 @@ namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  const int chunks = a.row_bytes / 16;                 // 16-byte chunks per (token, head) row
-  if (i >= (long long)a.total_new * a.Hkv * chunks) return;
-  const int c = (int)(i % chunks);
-  const long long r = i / chunks;
-  const int h = (int)(r % a.Hkv);
-  const int tok = (int)(r / a.Hkv);
+constexpr int kHeadGroup = 2;
+
+// Block: 256 threads = (256 / chunks) tokens x chunks 16-byte chunks; grid.y
+// runs over the head groups.
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a, int log2_chunks) {
+  const int c = threadIdx.x & ((1 << log2_chunks) - 1);
+  const int tok = blockIdx.x * (256 >> log2_chunks) + (threadIdx.x >> log2_chunks);
+  if (tok >= a.total_new) return;
   // sequence of the token: the largest b with cu_new[b] <= tok
   int lo = 0, hi = a.num_seqs;
   while (hi - lo > 1) {
@@ -37,23 +43,47 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   if (pos < 0 || pos >= a.max_pages * a.page_size) return;
   const int page = a.block_table[(size_t)b * a.max_pages + (pos >> a.log2_page)];
   if (page < 0 || page >= a.num_pages) return;
-  const size_t dst = (((size_t)page * a.Hkv + h) * a.page_size + (pos & (a.page_size - 1))) *
-                         a.row_bytes + (size_t)c * 16;
-  const size_t src = ((size_t)tok * a.Hkv + h) * a.row_bytes + (size_t)c * 16;
-  const u32x4_t kv = *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a.k_new) + src);
-  const u32x4_t vv = *reinterpret_cast<const u32x4_t *>(static_cast<const char *>(a.v_new) + src);
-  *reinterpret_cast<u32x4_t *>(static_cast<char *>(a.k_pool) + dst) = kv;
-  *reinterpret_cast<u32x4_t *>(static_cast<char *>(a.v_pool) + dst) = vv;
+  const int h0 = blockIdx.y * kHeadGroup;
+  const int nh = min(kHeadGroup, a.Hkv - h0);
+  const size_t rb = (size_t)a.row_bytes;
+  const size_t src = ((size_t)tok * a.Hkv + h0) * rb + c * 16;
+  const size_t dst = (((size_t)page * a.Hkv + h0) * a.page_size + (pos & (a.page_size - 1))) * rb +
+                     c * 16;
+  const size_t head_step = (size_t)a.page_size * rb;     // next head, same slot
+  const char *ks = static_cast<const char *>(a.k_new) + src;
+  const char *vs = static_cast<const char *>(a.v_new) + src;
+  char *kd = static_cast<char *>(a.k_pool) + dst;
+  char *vd = static_cast<char *>(a.v_pool) + dst;
+  u32x4_t kv[kHeadGroup], vv[kHeadGroup];
+#pragma unroll
+  for (int j = 0; j < kHeadGroup; ++j)
+    if (j < nh) {
+      kv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ks + j * rb));
+      vv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vs + j * rb));
+    }
+#pragma unroll
+  for (int j = 0; j < kHeadGroup; ++j)
+    if (j < nh) {
+      *reinterpret_cast<u32x4_t *>(kd + j * head_step) = kv[j];
+      *reinterpret_cast<u32x4_t *>(vd + j * head_step) = vv[j];
+    }
 }
 
 }  // namespace
 
 hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s) {
-  const long long threads = (long long)a.total_new * a.Hkv * (a.row_bytes / 16);
-  const long long blocks = (threads + 255) / 256;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  const int chunks = a.row_bytes / 16;
+  int log2_chunks = 0;
+  while ((1 << log2_chunks) < chunks) ++log2_chunks;
+  if (a.row_bytes % 16 != 0 || (1 << log2_chunks) != chunks || chunks > 256)
+    return hipErrorInvalidValue;
+  const int tokens_per_block = 256 >> log2_chunks;
+  const long long bx = ((long long)a.total_new + tokens_per_block - 1) / tokens_per_block;
+  const long long by = ((long long)a.Hkv + kHeadGroup - 1) / kHeadGroup;
+  if (bx <= 0 || by <= 0) return hipSuccess;
+  if (bx > 0x7fffffffLL || by > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, s, a,
+                     log2_chunks);
   return hipGetLastError();
 }
 
