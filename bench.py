@@ -148,7 +148,8 @@ def recorded_traffic(workload: str, kernel_source: str):
 def time_steps(step, steps: int, warmup: int, torch, min_warm_ms: float = 0.0):
     """Run warmup (at least `warmup` steps, and at least `min_warm_ms` of
     back-to-back work), then `steps` timed steps.  Returns (wall ms per
-    step, mean event ms per launch of the timed steps)."""
+    step, event-timed ms per step: the timed region's device time over the
+    steps, gaps between launches included)."""
     t0 = time.perf_counter()
     for _ in range(warmup):
         step()
@@ -158,16 +159,18 @@ def time_steps(step, steps: int, warmup: int, torch, min_warm_ms: float = 0.0):
             for _ in range(max(1, warmup)):
                 step()
             torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # one event pair around the whole timed region: an event pair around
+    # every step would put its own records between the launches
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         step()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
+    ev = start.elapsed_time(end) / steps
     return wall, ev
 
 
