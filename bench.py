@@ -389,7 +389,9 @@ def main():
         result = dict(base, metric=res["metric"], value=res["value"], unit="GB/s",
                       ms_per_step=res["ms_per_step"],
                       config={"workload": args.workload, "parallelism": "single GPU"},
-                      roofline=dict(res["roofline"], traffic=None, kernel="kv_append_kernel",
+                      roofline=dict(res["roofline"],
+                                    traffic=recorded_traffic(args.workload, "kv_append.hip"),
+                                    kernel="kv_append_kernel",
                                     kernel_ms=res["kernel_ms"],
                                     algorithmic_bytes=res["algorithmic_bytes"]))
         print(json.dumps(result), flush=True)
