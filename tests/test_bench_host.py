@@ -1,0 +1,66 @@
+"""Host-side checks of bench.py: the one-GPU guard and the timing loop."""
+import os
+import subprocess
+import sys
+import time
+import types
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+class _Event:
+    def __init__(self, log, enable_timing=False):
+        self.log = log
+        self.t = None
+
+    def record(self):
+        self.t = len(self.log)
+        self.log.append("event")
+
+    def elapsed_time(self, other):
+        # one "millisecond" per step launched between the two records
+        return float(sum(1 for x in self.log[self.t:other.t] if x == "step"))
+
+
+def _fake_torch(log):
+    cuda = types.SimpleNamespace(Event=lambda enable_timing=False: _Event(log, enable_timing),
+                                 synchronize=lambda: log.append("sync"))
+    return types.SimpleNamespace(cuda=cuda)
+
+
+def test_time_steps_brackets_exactly_the_timed_steps():
+    log = []
+    wall, ev = bench.time_steps(lambda: log.append("step"), steps=7, warmup=3,
+                                torch=_fake_torch(log))
+    assert log.count("step") == 10
+    assert log.count("event") == 2
+    first = log.index("event")
+    # warm-up steps all come before the first event, the timed ones between the two
+    assert log[:first].count("step") == 3
+    assert log[first:].count("step") == 7
+    assert ev == 1.0
+    assert wall >= 0.0
+
+
+def test_time_steps_warms_for_the_minimum_time():
+    log = []
+
+    def step():
+        log.append("step")
+        time.sleep(0.002)
+
+    bench.time_steps(step, steps=2, warmup=2, torch=_fake_torch(log), min_warm_ms=30.0)
+    first = log.index("event")
+    assert log[:first].count("step") >= 15       # at least 30 ms of 2 ms steps
+    assert log[first:].count("step") == 2
