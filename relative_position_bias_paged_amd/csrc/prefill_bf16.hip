@@ -17,8 +17,11 @@
 //  * 64-key K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4,
 //    no register staging) into two buffers, row-major with XOR-swizzled
 //    16-byte chunks: tile i+1 streams in while tile i computes, one barrier
-//    per tile.  Rows past the end of a sequence are filled from its last key
-//    (finite data whose probabilities are exactly zero);
+//    per tile.  Tile rows outside the work-group's key range (below the
+//    first key any of its queries sees, or past the end of the sequence)
+//    are filled from the nearest end of that range, so every K/V row loaded
+//    is a key some query of the call sees (finite data whose probabilities
+//    are exactly zero where it is masked);
 //  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16, so each
 //    lane owns one query column: the softmax row statistics stay in a lane
 //    pair (lane, lane^32);
@@ -37,8 +40,10 @@
 //  * three score paths chosen per wave and tile: clamp-only unmasked (scale,
 //    bias and max folded into one FMA before exp2), band unmasked, and a
 //    general path for window/causal/sequence-end edges and the clamp border;
-//  * masking selects (never multiplies), so NaN in keys past the end of a
-//    sequence or in masked positions cannot leak into the output;
+//  * masking selects (never multiplies), and no K/V row outside the keys the
+//    work-group's queries see is ever loaded, so pool slots no query may see
+//    (unwritten ring slots, pages past a sequence, keys older than the
+//    window) cannot reach the output whatever they hold;
 //  * the running max is rescaled lazily (only when a row's max grows by more
 //    than 2^8), which is exact because numerator and denominator share it.
 //
@@ -219,8 +224,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int R = a.R;
   const int W = a.window;
   const int p_last = hist + min(t0 + QM, L) - 1;   // position of the work-group's last query
-  int s_begin = (W > 0) ? max(0, hist + t0 - W + 1) : 0;
-  s_begin &= ~(BN - 1);
+  // first key any query of the work-group sees (its first query's window start)
+  const int s_first = (W > 0) ? max(0, hist + t0 - W + 1) : 0;
+  const int s_begin = s_first & ~(BN - 1);
 
   // Key tile s0 (a multiple of BN) against this wave's queries at positions
   // pq0..pq0+31, each test one compare with a per-wave bound (d = p - s
@@ -337,7 +343,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const long long v_minus_k = reinterpret_cast<const char *>(vp) - reinterpret_cast<const char *>(kp);
   const uint32_t page_bytes = (uint32_t)(page_stride * 2);   // checked on the host to fit
   auto load_kv = [&](int s0, int page_v, uint16_t *kl, uint16_t *vl) {
-    const int last = n_k - 1 - s0;      // rows above this repeat the last key
+    // Rows below `first` repeat the work-group's first visible key, rows
+    // above `last` the sequence's last key: only keys some query of the
+    // work-group sees are ever read (a 0 probability times a finite value is
+    // an exact 0 in the PV product; a non-finite one would not be).
+    const int first = s_first - s0;
+    const int last = n_k - 1 - s0;
     if constexpr (BIG_PAGE) {
       // the 64-key tile lies inside one page
       const uint32_t page = (uint32_t)__builtin_amdgcn_readfirstlane(page_v);
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const char *vt = kt + v_minus_k;
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const uint32_t ro = (uint32_t)min(dma_row[j], last) * (D * 2);
+        const uint32_t ro = (uint32_t)min(max(dma_row[j], first), last) * (D * 2);
         lds_void_t *kd = (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512);
         lds_void_t *vd = (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512);
         dma16(kt + (ro + k_off[j]), kd);
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     } else {
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j) {
-        const int sk = s0 + min(dma_row[j], last);
+        const int sk = s0 + min(max(dma_row[j], first), last);
         const size_t ko = ((size_t)trow[sk >> lp] * page_stride + (size_t)kvh * head_stride +
                            (size_t)(sk & (P - 1)) * D) * 2;
         lds_void_t *kd = (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512);

@@ -137,3 +137,21 @@ def oracle_decode(case: ri.DecodeCase, seqs=None, heads=None, want_lse=False):
         out, lse = res
         return (out.reshape(len(seqs), len(heads), -1), lse.reshape(len(seqs), len(heads)))
     return res.reshape(len(seqs), len(heads), -1)
+
+
+def sample_positions(L: int, count: int, gen: torch.Generator, window: int = 0,
+                     rel_extent: int = 0, offset: int = 0):
+    """Sorted query indices in [0, L): every tile and border case the kernels
+    special-case (sequence start and end, 32/64-query and 64-key tile edges,
+    the window edge, the clamp border t - s = R - 1 for the first key), then
+    random ones until ``count`` are chosen.  ``offset`` is the position of
+    index 0 (prefill over a history): borders are placed on positions."""
+    pos = {0, 1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 127, 128, 129, 191, 192, 255, 256}
+    for edge in (window, rel_extent):
+        if edge > 0:
+            pos |= {edge - 2, edge - 1, edge, edge + 1, edge + 63, edge + 64, 2 * edge - 1}
+    idx = {p - offset for p in pos} | {L - 65, L - 64, L - 33, L - 32, L - 2, L - 1}
+    idx = {i for i in idx if 0 <= i < L}
+    while len(idx) < min(count, L):
+        idx.add(int(torch.randint(0, L, (1,), generator=gen)))
+    return sorted(idx)

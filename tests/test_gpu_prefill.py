@@ -15,7 +15,7 @@ import torch
 
 import rba_inputs as ri
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, errors, gpu_prefill,
-                         oracle_prefill)
+                         oracle_prefill, sample_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -211,22 +211,76 @@ def test_zero_keys_bias_only_softmax(W, R, lens):
 @pytest.mark.parametrize("name", ["local-prefill-4x4096", "global-prefill-2x16384"])
 def test_full_size_workload_sampled(name):
     """The full-size prefill workloads, in the launch configuration the
-    benchmark times, checked on sampled rows (every sequence, every head,
-    first/last tokens, tile edges and random positions)."""
+    benchmark times, checked on sampled rows: every head of at least 128
+    tokens per sequence -- its first and last tokens, the 32/64-query and
+    64-key tile edges, the window edge and the clamp border t - s = R - 1,
+    and random positions."""
     dev = device()
     case = ri.build_workload(name, dev)["prefill"]
     out = gpu_prefill(case)
     torch.cuda.synchronize()
+    sp = case.spec
     g = torch.Generator().manual_seed(3)
     cu = case.cu_list()
     rows = []
-    for b in range(len(case.seq_lens)):
-        L = case.seq_lens[b]
-        ts = {0, 1, 63, 64, 127, 128, 511, 512, 1023, 1024, L - 2, L - 1}
-        ts |= set(torch.randint(0, L, (6,), generator=g).tolist())
-        for t in sorted(x for x in ts if 0 <= x < L):
-            h = int(torch.randint(0, case.spec.num_q_heads, (1,), generator=g))
-            rows.append((cu[b] + t, h))
+    for b, L in enumerate(case.seq_lens):
+        for t in sample_positions(L, 128, g, window=sp.window, rel_extent=sp.rel_extent):
+            rows += [(cu[b] + t, h) for h in range(sp.num_q_heads)]
+    assert len(rows) >= 128 * sp.num_q_heads * len(case.seq_lens)
     ref = oracle_prefill(case, rows=rows)
-    sel = torch.stack([out[tok, h] for tok, h in rows])
+    tok = torch.tensor([r[0] for r in rows], device=dev)
+    hd = torch.tensor([r[1] for r in rows], device=dev)
+    sel = out[tok, hd]
     assert_parity(sel, ref, torch.bfloat16, name)
+
+
+def _perturbed_pool(case, positions, seed):
+    """Copies of the case's K and V pools in which the keys at the given
+    logical positions (per sequence) hold other finite values: large ones
+    (|x| up to ~40) of either sign, so a leak would show."""
+    g = torch.Generator().manual_seed(seed)
+    k_pool, v_pool = case.k_pool.clone(), case.v_pool.clone()
+    table = case.block_table.cpu()
+    P = case.spec.page_size
+    for b, pos in enumerate(positions):
+        for s in pos:
+            page, slot = int(table[b, s // P]), s % P
+            shape = k_pool[page, :, slot, :].shape
+            k_pool[page, :, slot, :] = (torch.randn(shape, generator=g) * 13).to(k_pool.dtype).to(k_pool.device)
+            v_pool[page, :, slot, :] = (torch.randn(shape, generator=g) * 13).to(v_pool.dtype).to(v_pool.device)
+    return k_pool, v_pool
+
+
+@pytest.mark.parametrize("W,R", [(100, 100), (0, 256)])
+def test_masked_keys_inside_visible_tiles_have_no_effect(W, R):
+    """Finite changes to keys a row cannot see, inside tiles it partly sees,
+    leave that row bit-identical: future keys (after a cut position t0
+    that is not on a tile edge) for rows up to t0, and keys before a row's
+    window for rows whose window starts after them."""
+    dev = device()
+    sp = spec(8, 2, 128, W, R, 64)
+    lens = [700, 450]
+    case = ri.make_prefill(sp, lens, seed=29, device=dev, num_pages=20)
+    base = gpu_prefill(case)
+    cu = case.cu_list()
+    # future keys: positions after t0 in each sequence
+    t0 = [333, 161]
+    kf, vf = _perturbed_pool(case, [range(t + 1, n) for t, n in zip(t0, lens)], seed=1)
+    o_future = gpu_prefill(case, k_pool=kf, v_pool=vf)
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        a = base[cu[b]:cu[b] + t0[b] + 1].view(torch.int16)
+        c = o_future[cu[b]:cu[b] + t0[b] + 1].view(torch.int16)
+        assert torch.equal(a, c), f"future keys changed rows of sequence {b}"
+        # rows after t0 see the changed keys, so they must differ somewhere
+        assert not torch.equal(base[cu[b] + t0[b] + 1:cu[b + 1]], o_future[cu[b] + t0[b] + 1:cu[b + 1]])
+    if W > 0:
+        # keys before the window of rows t >= t1
+        t1 = [450, 321]
+        ko, vo = _perturbed_pool(case, [range(0, t - W + 1) for t in t1], seed=2)
+        o_old = gpu_prefill(case, k_pool=ko, v_pool=vo)
+        torch.cuda.synchronize()
+        for b in range(len(lens)):
+            a = base[cu[b] + t1[b]:cu[b + 1]].view(torch.int16)
+            c = o_old[cu[b] + t1[b]:cu[b + 1]].view(torch.int16)
+            assert torch.equal(a, c), f"keys before the window changed rows of sequence {b}"

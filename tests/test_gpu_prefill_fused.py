@@ -19,7 +19,7 @@ import torch
 
 import rba_inputs as ri
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, errors, gpu_prefill,
-                         gpu_prefill_fused, oracle_prefill_projected)
+                         gpu_prefill_fused, oracle_prefill_projected, sample_positions)
 import relative_position_bias_paged_amd as rba
 
 pytestmark = pytest.mark.gpu
@@ -105,25 +105,24 @@ def test_fused_null_seq_lens_is_plain_prefill():
                                   "fused-global-prefill-2x16384-drel32"])
 def test_fused_workload_sampled(name):
     """The fused benchmark workloads at full size, in the launch the bench
-    times, checked on sampled rows: every sequence, its first and last
-    tokens, tile and clamp borders, and random ones."""
+    times, checked on every head of at least 128 tokens per sequence: its
+    first and last tokens, tile, window and clamp borders, and random ones."""
     dev = device()
     case = ri.build_workload(name, dev)["prefill"]
     out = gpu_prefill_fused(case)
     torch.cuda.synchronize()
     h = case.hist
+    sp = h.spec
     g = torch.Generator().manual_seed(11)
     cu = h.cu_list()
-    R = h.spec.rel_extent
     rows = []
     for b, L in enumerate(h.new_lens):
-        ts = {0, 1, 63, 64, 511, 512, R - 1, R, R + 63, L - 2, L - 1}
-        ts |= set(torch.randint(0, L, (6,), generator=g).tolist())
-        for t in sorted(x for x in ts if 0 <= x < L):
-            rows.append((cu[b] + t, int(torch.randint(0, h.spec.num_q_heads, (1,), generator=g))))
+        for t in sample_positions(L, 128, g, window=sp.window, rel_extent=sp.rel_extent):
+            rows += [(cu[b] + t, hh) for hh in range(sp.num_q_heads)]
     ref = oracle_prefill_projected(case, rows=rows)
-    sel = torch.stack([out[tok, hh] for tok, hh in rows])
-    assert_parity(sel, ref, torch.bfloat16, name)
+    tok = torch.tensor([r[0] for r in rows], device=dev)
+    hd = torch.tensor([r[1] for r in rows], device=dev)
+    assert_parity(out[tok, hd], ref, torch.bfloat16, name)
 
 
 def test_fused_rejects_fp32_pools():

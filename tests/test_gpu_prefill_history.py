@@ -16,7 +16,7 @@ import torch
 
 import rba_inputs as ri
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, errors, gpu_decode, gpu_prefill,
-                         oracle_prefill_history)
+                         oracle_prefill_history, sample_positions)
 import relative_position_bias_paged_amd as rba
 
 pytestmark = pytest.mark.gpu
@@ -123,20 +123,23 @@ def test_null_seq_lens_is_plain_prefill():
 
 @pytest.mark.parametrize("name", ["chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384"])
 def test_chunked_workload_sampled(name):
-    """The chunked-prefill benchmark workloads at full size, checked on sampled
-    rows (every sequence, first/last new tokens, tile edges, random ones)."""
+    """The chunked-prefill benchmark workloads at full size, checked on every
+    head of at least 128 new tokens per sequence: the first and last new
+    tokens, tile edges, window and clamp borders (on positions), and random
+    ones."""
     dev = device()
     case = ri.build_workload(name, dev)["prefill"]
     out = gpu_prefill(case)
     torch.cuda.synchronize()
+    sp = case.spec
     g = torch.Generator().manual_seed(5)
     cu = case.cu_list()
     rows = []
-    for b, L in enumerate(case.new_lens):
-        ts = {0, 1, 63, 64, 127, 128, L - 2, L - 1}
-        ts |= set(torch.randint(0, L, (6,), generator=g).tolist())
-        for t in sorted(x for x in ts if 0 <= x < L):
-            rows.append((cu[b] + t, int(torch.randint(0, case.spec.num_q_heads, (1,), generator=g))))
+    for b, (n, L) in enumerate(zip(case.key_lens, case.new_lens)):
+        for t in sample_positions(L, 128, g, window=sp.window, rel_extent=sp.rel_extent,
+                                  offset=n - L):
+            rows += [(cu[b] + t, h) for h in range(sp.num_q_heads)]
     ref = oracle_prefill_history(case, rows=rows)
-    sel = torch.stack([out[tok, h] for tok, h in rows])
-    assert_parity(sel, ref, torch.bfloat16, name)
+    tok = torch.tensor([r[0] for r in rows], device=dev)
+    hd = torch.tensor([r[1] for r in rows], device=dev)
+    assert_parity(out[tok, hd], ref, torch.bfloat16, name)

@@ -1,7 +1,8 @@
 """Window-only local pools: each sequence owns a ring of
 rba_window_ring_pages(window, page_size, max_new) pages, and its positional
 block table maps page j to ring[j % ring_pages].  Keys older than the window
-are overwritten as the sequence grows; the kernels never read them.
+are overwritten as the sequence grows; the kernels never read them (nor the
+ring slots no query of a call sees, whatever they hold).
 
 Checked on the GPU against the oracle on the full logical keys: a local
 layer prefilled chunk by chunk (append, then prefill over the history) into
@@ -104,3 +105,72 @@ def test_decode_steps_through_a_ring():
         assert_parity(out, ref, torch.bfloat16, f"ring decode step {s}")
     # the pool is O(window): ring pages per sequence, whatever the length
     assert k_pool.shape[0] == B * ring
+
+
+@pytest.mark.parametrize("P", [16, 64])
+@pytest.mark.parametrize("new", [1, 4])
+def test_prefill_new_tokens_through_a_window_only_ring(P, new):
+    """Prefill of a few new tokens over a ring that holds only the keys the
+    call's queries can see (the rest of the ring is NaN, as after a fresh
+    allocation).  Window starts fall off the 64-key tile.  The result matches
+    the oracle on the full logical keys and is bit-identical to the same call
+    on a twin ring whose unwritten slots hold zeros."""
+    dev = device()
+    W, R, Hq, Hkv, D = 512, 512, 8, 2, 128
+    sp = ri.LayerSpec(num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, window=W, rel_extent=R,
+                      page_size=P)
+    lens = [5000, 777, 1300, 515]
+    B = len(lens)
+    case = ri.make_prefill_history(sp, lens, [new] * B, seed=90 + P + new, device="cpu")
+    ring = rba.window_ring_pages(W, P, new)
+    rings = _rings(B, ring, dev, seed=P * 10 + new)
+    table = rba.ring_block_table(rings, -(-max(lens) // P))
+    k_pool = torch.full((B * ring, Hkv, P, D), float("nan"), dtype=sp.dtype, device=dev)
+    v_pool = torch.full_like(k_pool, float("nan"))
+    # the keys the call's queries see: positions n - new - W + 1 .. n - 1
+    cu_kv = case.cu_kv_list()
+    lo = [max(0, n - new - W + 1) for n in lens]
+    rows = torch.cat([torch.arange(cu_kv[b] + lo[b], cu_kv[b + 1]) for b in range(B)])
+    assert any((n - new - W + 1) % 64 for n in lens)
+    seq_lens = torch.tensor(lens, dtype=torch.int32, device=dev)
+    rba.kv_append(case.k_log[rows].to(dev), case.v_log[rows].to(dev),
+                  torch.tensor(ri._cumsum([n - l for n, l in zip(lens, lo)]), dtype=torch.int32,
+                               device=dev),
+                  k_pool, v_pool, table, seq_lens)
+    assert torch.isnan(k_pool).any()
+    q, bias = case.q.to(dev), case.bias.to(dev)
+    cu_q = torch.tensor(case.cu_list(), dtype=torch.int32, device=dev)
+    o_nan = rba.prefill(q, cu_q, new, k_pool, v_pool, table, seq_lens, bias, window=W,
+                        sm_scale=sp.scale())
+    o_zero = rba.prefill(q, cu_q, new, torch.nan_to_num(k_pool, nan=0.0),
+                         torch.nan_to_num(v_pool, nan=0.0), table, seq_lens, bias, window=W,
+                         sm_scale=sp.scale())
+    torch.cuda.synchronize()
+    ref = oracle.prefill_history(case.q, case.k_log, case.v_log, case.bias, case.cu_list(),
+                                 cu_kv, window=W, rel_extent=R, sm_scale=sp.scale())
+    assert_parity(o_nan, ref, torch.bfloat16, f"ring prefill P={P} new={new}")
+    assert torch.equal(o_nan.view(torch.int16), o_zero.view(torch.int16))
+
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_prefill_last_token_on_a_window_only_decode_pool(P):
+    """One new token through rba_prefill on a window-only pool (every table
+    entry before the window's first page points at one NaN page) equals
+    rba_decode on the same pool, and both match the oracle."""
+    dev = device()
+    sp = ri.LayerSpec(num_q_heads=8, num_kv_heads=2, head_dim=128, window=300, rel_extent=300,
+                      page_size=P)
+    lens = [5000, 777, 301, 64, 1]
+    case = ri.make_decode(sp, lens, seed=40 + P, device=dev, window_only=True)
+    assert torch.isnan(case.k_pool[0]).all()
+    cu = torch.arange(len(lens) + 1, dtype=torch.int32, device=dev)
+    o_pre = rba.prefill(case.q, cu, 1, case.k_pool, case.v_pool, case.block_table,
+                        case.seq_lens_dev, case.bias, window=sp.window, sm_scale=sp.scale())
+    o_dec = rba.decode(case.q, case.k_pool, case.v_pool, case.block_table, case.seq_lens_dev,
+                       case.max_seq_len, case.bias, window=sp.window, sm_scale=sp.scale())
+    torch.cuda.synchronize()
+    ks, vs = zip(*(case.logical_kv(b) for b in range(len(lens))))
+    ref = oracle.decode(case.q, torch.cat(ks), torch.cat(vs), case.bias, ri._cumsum(lens),
+                        window=sp.window, rel_extent=sp.rel_extent, sm_scale=sp.scale())
+    assert_parity(o_pre, ref, torch.bfloat16, f"prefill on window pool P={P}")
+    assert_parity(o_dec, ref, torch.bfloat16, f"decode on window pool P={P}")
