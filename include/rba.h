@@ -186,6 +186,12 @@ int32_t rba_decode_num_splits(const rba_kv_cache *kv, const rba_page_table *pt,
 /*
  * Bytes of device workspace rba_decode needs for these arguments (0 when it
  * runs without partitions).  Returns 0 on invalid arguments as well.
+ *
+ * The arguments are those of the decode call itself (the pool and page
+ * table, max_seq_len and the layer parameters), not only (num_seqs, Hq,
+ * head_dim, num_splits): with num_splits == 0 the partition count is
+ * planned from max_seq_len, the page size and the window, and the workspace
+ * also holds the largest-first order of the (sequence, partition) items.
  */
 size_t rba_decode_workspace_size(const rba_kv_cache *kv,
                                  const rba_page_table *pt, int32_t max_seq_len,
@@ -194,7 +200,13 @@ size_t rba_decode_workspace_size(const rba_kv_cache *kv,
 
 /*
  * Single-token decode: one query per sequence at position seq_lens[b] - 1,
- * attending the seq_lens[b] keys in the pool (its own key included).  With
+ * attending the seq_lens[b] keys in the pool (its own key included).  The
+ * score is the one of rba_prefill (TensorRT-LLM PR #17062 page, Description,
+ * Architecture list); the key count per sequence comes from the cache, as in
+ * the TensorRT-LLM PR #17860 page's commit moving the model onto the
+ * framework's hooks (the KV lengths are the cached token counts), and keys
+ * are read through the positional page table of that page's commit that
+ * borrows the framework page table.  With
  * more than one partition the visible key range of each sequence is cut into
  * page-aligned partitions, each partition's normalised partial output and
  * log-sum-exp go to the workspace, and a second kernel merges them with
@@ -211,7 +223,10 @@ size_t rba_decode_workspace_size(const rba_kv_cache *kv,
  *              aligned (may be NULL when that size is 0); contents on entry
  *              are ignored
  *  out         [num_seqs][Hq][head_dim] (written)
- *  lse         NULL or float [num_seqs][Hq] (written)
+ *  lse         NULL or float [num_seqs][Hq] (written): natural-log sum of
+ *              exp(score) over the visible keys, the quantity the split-K
+ *              merge combines; callers that merge further (e.g. partial
+ *              results from several devices) need it
  *
  * Errors as for rba_prefill, plus RBA_ERR_WORKSPACE.  A sequence with
  * seq_lens[b] == 0 gets a zero output row and lse = -inf.
@@ -267,6 +282,18 @@ rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu
  * size that is not a power of two, or max_new < 1.  Host only.
  */
 int32_t rba_window_ring_pages(int32_t window, int32_t page_size, int32_t max_new);
+
+/*
+ * The positional block table of a window-only pool (rba_window_ring_pages):
+ * block_table[b][j] = rings[b][j % ring_pages] for j < max_pages_per_seq.
+ * HOST memory: rings int32 [num_seqs][ring_pages], block_table int32
+ * [num_seqs][max_pages_per_seq] (written; the caller copies it to the
+ * device).  The table is caller metadata built once per sequence; no kernel
+ * is involved.  RBA_ERR_INVALID_ARG for a negative count, ring_pages < 1 or a
+ * null pointer with a non-empty table.
+ */
+rba_status rba_ring_block_table(const int32_t *rings, int32_t num_seqs, int32_t ring_pages,
+                                int32_t max_pages_per_seq, int32_t *block_table);
 
 /* Static, human-readable name of a status code. */
 const char *rba_status_string(rba_status status);

@@ -16,8 +16,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_size",
-           "status_string", "RbaError", "library_path", "load"]
+__all__ = ["prefill", "prefill_fused", "decode", "decode_num_splits", "decode_workspace_size",
+           "kv_append", "window_ring_pages", "ring_block_table", "status_string", "RbaError",
+           "library_path", "load"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librba.so")
@@ -34,7 +35,7 @@ RBA_F32 = 1
 # every symbol include/rba.h declares
 EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_num_splits",
             "rba_decode_workspace_size", "rba_kv_append", "rba_window_ring_pages",
-            "rba_status_string")
+            "rba_ring_block_table", "rba_status_string")
 
 
 class rba_page_table(ctypes.Structure):
@@ -101,6 +102,9 @@ def load():
                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
     lib.rba_decode.restype = ctypes.c_int
+    lib.rba_ring_block_table.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_void_p]
+    lib.rba_ring_block_table.restype = ctypes.c_int
     lib.rba_decode_num_splits.argtypes = [P(rba_kv_cache), P(rba_page_table), ctypes.c_int32,
                                           P(rba_attn_params), ctypes.c_int32]
     lib.rba_decode_num_splits.restype = ctypes.c_int32
@@ -274,14 +278,18 @@ def window_ring_pages(window: int, page_size: int, max_new: int = 1) -> int:
 
 
 def ring_block_table(rings: torch.Tensor, max_pages_per_seq: int) -> torch.Tensor:
-    """Positional block table over per-sequence page rings: entry j of
-    sequence b is rings[b][j % ring_pages].  rings: int32 [num_seqs,
-    ring_pages] (any device); returns int32 [num_seqs, max_pages_per_seq] on
-    the same device.  Host-side index arithmetic only."""
+    """rba_ring_block_table: the positional block table over per-sequence
+    page rings, entry j of sequence b = rings[b][j % ring_pages].  rings:
+    int32 [num_seqs, ring_pages] (any device; the C helper runs on a host
+    copy); returns int32 [num_seqs, max_pages_per_seq] on the same device."""
     if rings.dim() != 2 or rings.dtype != torch.int32:
         raise ValueError("rings must be int32 [num_seqs, ring_pages]")
-    j = torch.arange(max_pages_per_seq, device=rings.device) % rings.shape[1]
-    return rings[:, j].contiguous()
+    host = rings.detach().to("cpu").contiguous()
+    table = torch.empty((host.shape[0], int(max_pages_per_seq)), dtype=torch.int32)
+    st = load().rba_ring_block_table(host.data_ptr(), host.shape[0], host.shape[1],
+                                     int(max_pages_per_seq), table.data_ptr())
+    _check(st, "rba_ring_block_table")
+    return table.to(rings.device)
 
 
 def _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale):
@@ -341,3 +349,4 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                         _dev(out, "out"), lse_ptr, _stream(stream))
     _check(st, "rba_decode")
     return out
+

@@ -274,6 +274,18 @@ RBA_EXPORT int32_t rba_window_ring_pages(int32_t window, int32_t page_size, int3
   return pages > 0x7fffffffLL ? 0 : (int32_t)pages;
 }
 
+RBA_EXPORT rba_status rba_ring_block_table(const int32_t *rings, int32_t num_seqs,
+                                           int32_t ring_pages, int32_t max_pages_per_seq,
+                                           int32_t *block_table) {
+  if (num_seqs < 0 || ring_pages < 1 || max_pages_per_seq < 0) return RBA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_pages_per_seq == 0) return RBA_OK;
+  if (rings == nullptr || block_table == nullptr) return RBA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < num_seqs; ++b)
+    for (int32_t j = 0; j < max_pages_per_seq; ++j)
+      block_table[(size_t)b * max_pages_per_seq + j] = rings[(size_t)b * ring_pages + j % ring_pages];
+  return RBA_OK;
+}
+
 RBA_EXPORT int32_t rba_decode_num_splits(const rba_kv_cache *kv, const rba_page_table *pt,
                                          int32_t max_seq_len, const rba_attn_params *params,
                                          int32_t num_splits) {

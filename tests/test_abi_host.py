@@ -265,6 +265,23 @@ def test_ring_block_table_is_positional():
     rings = torch.tensor([[7, 3, 9], [0, 1, 2]], dtype=torch.int32)
     t = rba.ring_block_table(rings, 8)
     assert t.tolist() == [[7, 3, 9, 7, 3, 9, 7, 3], [0, 1, 2, 0, 1, 2, 0, 1]]
+    # against the definition, on a larger random ring set
+    g = torch.Generator().manual_seed(1)
+    rings = torch.randperm(5 * 9, generator=g).to(torch.int32).view(5, 9)
+    t = rba.ring_block_table(rings, 40)
+    for b in range(5):
+        for j in range(40):
+            assert int(t[b, j]) == int(rings[b, j % 9])
+
+
+def test_ring_block_table_errors():
+    lib = rba.load()
+    buf = (ctypes.c_int32 * 8)()
+    assert lib.rba_ring_block_table(buf, 2, 0, 4, buf) == rba.RBA_ERR_INVALID_ARG
+    assert lib.rba_ring_block_table(buf, -1, 3, 4, buf) == rba.RBA_ERR_INVALID_ARG
+    assert lib.rba_ring_block_table(None, 2, 3, 4, buf) == rba.RBA_ERR_INVALID_ARG
+    assert lib.rba_ring_block_table(buf, 2, 3, 4, None) == rba.RBA_ERR_INVALID_ARG
+    assert lib.rba_ring_block_table(None, 0, 3, 4, None) == rba.RBA_OK
 
 
 def test_status_strings():
