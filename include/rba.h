@@ -33,7 +33,8 @@
  *    that holds a key below seq_len).
  *  - Tensor pointers must be 16-byte aligned; all tensors are contiguous,
  *    row-major in the shapes given.
- *  - No C++ exception crosses the ABI.  The library holds no mutable global
+ *  - No C++ exception crosses the ABI.  Apart from rba_decode_noalloc's
+ *    per-device workspace (see there), the library holds no mutable global
  *    state; calls on different streams may run concurrently.
  */
 #ifndef RBA_H
@@ -237,6 +238,35 @@ rba_status rba_decode(const void *q, const rba_kv_cache *kv,
                       int32_t num_splits, void *workspace,
                       size_t workspace_bytes, void *out, float *lse,
                       hipStream_t stream);
+
+/* Largest workspace rba_decode_noalloc can use: 64 MiB per GPU. */
+#define RBA_DECODE_SCRATCH_BYTES (64u << 20)
+
+/*
+ * rba_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation, kernels and results as rba_decode, with the workspace
+ * taken from a static device array of RBA_DECODE_SCRATCH_BYTES that every
+ * GPU the library runs on holds until the process ends.  The call allocates
+ * and frees nothing; its first call on a device looks up that device's
+ * array (work must be enqueued on a stream of the current device).
+ *
+ * Every call on one GPU shares that GPU's array, so calls that may overlap
+ * on one GPU (different streams, or different host threads) race: order
+ * them.  Nothing in the array needs to start at zero (every byte read in a
+ * call is written earlier in the same call), so the previous call's
+ * contents are harmless.
+ *
+ * Arguments and errors as rba_decode without the workspace; a call whose
+ * workspace (rba_decode_workspace_size) would exceed RBA_DECODE_SCRATCH_BYTES
+ * returns RBA_ERR_WORKSPACE before anything is enqueued (fewer partitions,
+ * or rba_decode with a caller workspace, fit such a call).
+ */
+rba_status rba_decode_noalloc(const void *q, const rba_kv_cache *kv,
+                              const rba_page_table *pt, int32_t max_seq_len,
+                              const void *bias, const rba_attn_params *params,
+                              int32_t num_splits, void *out, float *lse,
+                              hipStream_t stream);
 
 /*
  * Append: write the keys and values of new tokens into their pool pages, so

@@ -16,9 +16,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "prefill_fused", "decode", "decode_num_splits", "decode_workspace_size",
-           "kv_append", "window_ring_pages", "ring_block_table", "status_string", "RbaError",
-           "library_path", "load"]
+__all__ = ["prefill", "prefill_fused", "decode", "decode_noalloc", "decode_num_splits",
+           "decode_workspace_size", "kv_append", "window_ring_pages", "ring_block_table",
+           "status_string", "RbaError", "library_path", "load", "DECODE_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librba.so")
@@ -33,9 +33,12 @@ RBA_BF16 = 0
 RBA_F32 = 1
 
 # every symbol include/rba.h declares
-EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_num_splits",
-            "rba_decode_workspace_size", "rba_kv_append", "rba_window_ring_pages",
-            "rba_ring_block_table", "rba_status_string")
+EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_noalloc",
+            "rba_decode_num_splits", "rba_decode_workspace_size", "rba_kv_append",
+            "rba_window_ring_pages", "rba_ring_block_table", "rba_status_string")
+
+# RBA_DECODE_SCRATCH_BYTES of include/rba.h: the workspace limit of rba_decode_noalloc
+DECODE_SCRATCH_BYTES = 64 << 20
 
 
 class rba_page_table(ctypes.Structure):
@@ -102,6 +105,11 @@ def load():
                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.c_void_p]
     lib.rba_decode.restype = ctypes.c_int
+    lib.rba_decode_noalloc.argtypes = [ctypes.c_void_p, P(rba_kv_cache), P(rba_page_table),
+                                       ctypes.c_int32, ctypes.c_void_p, P(rba_attn_params),
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
+    lib.rba_decode_noalloc.restype = ctypes.c_int
     lib.rba_ring_block_table.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_void_p]
     lib.rba_ring_block_table.restype = ctypes.c_int
@@ -350,3 +358,29 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
     _check(st, "rba_decode")
     return out
 
+
+def decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                   block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                   bias: torch.Tensor, *, window: int, sm_scale: float, out: torch.Tensor,
+                   num_splits: int = 0, lse: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """rba_decode_noalloc: rba_decode with its workspace in the library's
+    static per-GPU array (at most DECODE_SCRATCH_BYTES).  ``out`` (and
+    ``lse``) are the caller's: nothing is allocated here or in the call.
+    Calls that may overlap on one GPU race on that array."""
+    lib = load()
+    kv, pt, prm = _decode_structs(q, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale)
+    if q.dtype != k_pool.dtype or bias.dtype != k_pool.dtype:
+        raise TypeError("q, bias and the pools must share one dtype")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lse_ptr = None
+    if lse is not None:
+        if lse.shape != q.shape[:2]:
+            raise ValueError("lse must be [B, Hq]")
+        lse_ptr = _dev(lse, "lse", torch.float32)
+    st = lib.rba_decode_noalloc(_dev(q, "q"), ctypes.byref(kv), ctypes.byref(pt),
+                                int(max_seq_len), _dev(bias, "bias"), ctypes.byref(prm),
+                                int(num_splits), _dev(out, "out"), lse_ptr, _stream(stream))
+    _check(st, "rba_decode_noalloc")
+    return out

@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "rba_internal.h"
 
@@ -301,14 +302,18 @@ RBA_EXPORT size_t rba_decode_workspace_size(const rba_kv_cache *kv, const rba_pa
   return workspace_bytes_for(kv, pt, params, sp.splits);
 }
 
-RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
-                                 int32_t max_seq_len, const void *bias,
-                                 const rba_attn_params *params, int32_t num_splits,
-                                 void *workspace, size_t workspace_bytes, void *out, float *lse,
-                                 hipStream_t stream) {
+namespace {
+
+// Host-side checks of a decode call.  On RBA_OK, *sp holds the partition
+// plan and *need the workspace bytes it takes (0 without partitions).
+rba_status decode_check(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
+                        int32_t max_seq_len, const void *bias, const rba_attn_params *params,
+                        int32_t num_splits, void *out, float *lse, SplitPlan *sp, size_t *need) {
   rba_status st = check_layer(kv, pt, params);
   if (st != RBA_OK) return st;
   if (max_seq_len < 0 || num_splits < 0) return RBA_ERR_INVALID_ARG;
+  *sp = plan_splits(kv, pt, max_seq_len, params, num_splits);
+  *need = 0;
   if (pt->num_seqs == 0) return RBA_OK;
   if (q == nullptr || bias == nullptr || out == nullptr || pt->seq_lens == nullptr)
     return RBA_ERR_INVALID_ARG;
@@ -317,15 +322,15 @@ RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rb
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
   if ((long long)max_seq_len > (long long)pt->max_pages_per_seq * pt->page_size)
     return RBA_ERR_INVALID_ARG;
+  *need = workspace_bytes_for(kv, pt, params, sp->splits);
+  return RBA_OK;
+}
 
-  const SplitPlan sp = plan_splits(kv, pt, max_seq_len, params, num_splits);
-  const size_t need = workspace_bytes_for(kv, pt, params, sp.splits);
-  if (need > 0) {
-    if (workspace == nullptr || workspace_bytes < need ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return RBA_ERR_WORKSPACE;
-  }
-
+// Enqueues a checked decode call (decode_check returned RBA_OK).
+rba_status decode_launch(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
+                         const void *bias, const rba_attn_params *params, const SplitPlan &sp,
+                         size_t need, void *workspace, void *out, float *lse,
+                         hipStream_t stream) {
   rba::DecodeArgs a{};
   a.q = q;
   a.k_pool = kv->k_pool;
@@ -375,4 +380,69 @@ RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rb
     if (err == hipSuccess && sp.splits > 1) err = rba::launch_merge(a, kv->head_dim, true, stream);
   }
   return err == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}
+
+}  // namespace
+
+// Workspace of rba_decode_noalloc: one static array per GPU, held until the
+// process ends.  Host code never uses its name as an address (in host code
+// it is a stand-in, not device memory): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[RBA_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_addr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+hipError_t scratch_for_current_device(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    void *p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    scratch_addr[dev] = scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = scratch_addr[dev];
+  return scratch_err[dev];
+}
+
+}  // namespace
+
+RBA_EXPORT rba_status rba_decode(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
+                                 int32_t max_seq_len, const void *bias,
+                                 const rba_attn_params *params, int32_t num_splits,
+                                 void *workspace, size_t workspace_bytes, void *out, float *lse,
+                                 hipStream_t stream) {
+  SplitPlan sp;
+  size_t need;
+  const rba_status st =
+      decode_check(q, kv, pt, max_seq_len, bias, params, num_splits, out, lse, &sp, &need);
+  if (st != RBA_OK || pt->num_seqs == 0) return st;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return RBA_ERR_WORKSPACE;
+  }
+  return decode_launch(q, kv, pt, bias, params, sp, need, workspace, out, lse, stream);
+}
+
+RBA_EXPORT rba_status rba_decode_noalloc(const void *q, const rba_kv_cache *kv,
+                                         const rba_page_table *pt, int32_t max_seq_len,
+                                         const void *bias, const rba_attn_params *params,
+                                         int32_t num_splits, void *out, float *lse,
+                                         hipStream_t stream) {
+  SplitPlan sp;
+  size_t need;
+  const rba_status st =
+      decode_check(q, kv, pt, max_seq_len, bias, params, num_splits, out, lse, &sp, &need);
+  if (st != RBA_OK || pt->num_seqs == 0) return st;
+  if (need > (size_t)RBA_DECODE_SCRATCH_BYTES) return RBA_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need > 0 && scratch_for_current_device(&ws) != hipSuccess) return RBA_ERR_HIP;
+  return decode_launch(q, kv, pt, bias, params, sp, need, ws, out, lse, stream);
 }

@@ -284,6 +284,39 @@ def test_ring_block_table_errors():
     assert lib.rba_ring_block_table(None, 0, 3, 4, None) == rba.RBA_OK
 
 
+def _decode_noalloc(kv, pt, prm, q=FAKE, max_len=1000, bias=FAKE, splits=0, out=FAKE, lse=None):
+    return rba.load().rba_decode_noalloc(q, ctypes.byref(kv), ctypes.byref(pt), max_len, bias,
+                                         ctypes.byref(prm), splits, out, lse, None)
+
+
+def test_decode_noalloc_host_checks():
+    """The allocation-free decode shares rba_decode's checks and rejects a call
+    whose workspace would not fit the static per-GPU array, before any
+    device work (so these run without a GPU)."""
+    kv, pt, prm = _layer(hq=30, hkv=8)
+    assert _decode_noalloc(kv, pt, prm) == rba.RBA_ERR_INVALID_ARG
+    kv, pt, prm = _layer()
+    assert _decode_noalloc(kv, pt, prm, q=0) == rba.RBA_ERR_INVALID_ARG
+    kv, pt, prm = _layer(lens=0)
+    assert _decode_noalloc(kv, pt, prm) == rba.RBA_ERR_INVALID_ARG
+    # 1024 sequences x 32 heads x 64 partitions of fp32 partials: 1 GiB
+    kv, pt, prm = _layer(seqs=1024, max_pages=2048, pages=1 << 20)
+    lib = rba.load()
+    need = lib.rba_decode_workspace_size(ctypes.byref(kv), ctypes.byref(pt), 131072,
+                                         ctypes.byref(prm), 64)
+    assert need > rba.DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(kv, pt, prm, max_len=131072, splits=64) == rba.RBA_ERR_WORKSPACE
+    kv, pt, prm = _layer(seqs=0)
+    assert _decode_noalloc(kv, pt, prm, q=0, bias=0, out=0) == rba.RBA_OK
+
+
+def test_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    import re as _re
+    m = _re.search(r"#define RBA_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == rba.DECODE_SCRATCH_BYTES
+
+
 def test_status_strings():
     for code, name in [(0, "RBA_OK"), (1, "RBA_ERR_INVALID_ARG"), (2, "RBA_ERR_UNSUPPORTED"),
                        (3, "RBA_ERR_WORKSPACE"), (4, "RBA_ERR_HIP")]:
