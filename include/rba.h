@@ -269,6 +269,48 @@ rba_status rba_decode_noalloc(const void *q, const rba_kv_cache *kv,
                               hipStream_t stream);
 
 /*
+ * Decode of q_len new tokens per sequence at once (q_len 1..16), the pass
+ * that verifies the drafted tokens of a multi-token-prediction step (the
+ * vLLM PR #48768 "Add Inkling multi-depth MTP support [5/N]" page: the
+ * target model checks every depth's drafts in one forward pass).  Sequence
+ * b holds n_b = seq_lens[b] keys, the keys of its q_len new tokens included
+ * (a value below q_len is read as q_len); token b*q_len + i sits at position
+ * n_b - q_len + i and attends the keys before it as in rba_prefill over a
+ * history.  The result equals that prefill's; the work is split as in
+ * rba_decode: page-aligned partitions of the keys any of the sequence's
+ * queries sees, one pass that writes each partition's normalised partial
+ * output and log-sum-exp, and the merge.  Each K/V tile is loaded once for
+ * all the sequence's tokens of up to 16 / q_len query heads.
+ *
+ *  q           [num_seqs * q_len][Hq][head_dim], sequence b's tokens at rows
+ *              b*q_len .. b*q_len + q_len - 1
+ *  q_len       tokens per sequence, 1 .. 16 (1 is rba_decode)
+ *  bias        [num_seqs * q_len][Hq][rel_extent]: each token's own row
+ *  out         [num_seqs * q_len][Hq][head_dim] (written)
+ *  lse         NULL or float [num_seqs * q_len][Hq] (written)
+ *  workspace   rba_decode_multi_workspace_size() bytes, 256-byte aligned
+ *              (NULL when that is 0); contents on entry are ignored
+ *
+ * Errors as rba_decode; RBA_ERR_UNSUPPORTED for q_len > 16, and for fp32
+ * pools with q_len > 1 (rba_prefill over a history computes those).
+ */
+rba_status rba_decode_multi(const void *q, int32_t q_len, const rba_kv_cache *kv,
+                            const rba_page_table *pt, int32_t max_seq_len,
+                            const void *bias, const rba_attn_params *params,
+                            int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, void *out, float *lse,
+                            hipStream_t stream);
+
+/* Partition count and workspace bytes of rba_decode_multi (0 on invalid
+ * arguments), as rba_decode_num_splits / rba_decode_workspace_size. */
+int32_t rba_decode_multi_num_splits(int32_t q_len, const rba_kv_cache *kv,
+                                    const rba_page_table *pt, int32_t max_seq_len,
+                                    const rba_attn_params *params, int32_t num_splits);
+size_t rba_decode_multi_workspace_size(int32_t q_len, const rba_kv_cache *kv,
+                                       const rba_page_table *pt, int32_t max_seq_len,
+                                       const rba_attn_params *params, int32_t num_splits);
+
+/*
  * Append: write the keys and values of new tokens into their pool pages, so
  * that a following rba_prefill or rba_decode reads them.  Sequence b holds
  * n_b = pt->seq_lens[b] keys after the call, and its L_b new tokens

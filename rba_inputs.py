@@ -81,6 +81,9 @@ class PrefillCase:
 
 @dataclasses.dataclass
 class DecodeCase:
+    """Decode inputs.  q and bias hold q_len rows per sequence (row b*q_len
+    + i is sequence b's token at position n_b - q_len + i); q_len 1 is the
+    single-token decode, [B, Hq, D] / [B, Hq, R]."""
     spec: LayerSpec
     seq_lens: List[int]
     q: torch.Tensor
@@ -92,6 +95,7 @@ class DecodeCase:
     seed: int
     window_only: bool
     _kv_first_page: List[int]     # first page index whose contents are real
+    q_len: int = 1
 
     @property
     def max_seq_len(self) -> int:
@@ -356,25 +360,27 @@ def _seq_kv(spec: LayerSpec, seed: int, b: int, n: int, device):
 
 
 def make_decode(spec: LayerSpec, seq_lens: List[int], seed: int, device="cpu",
-                window_only: bool = False, shuffle: bool = True) -> DecodeCase:
-    """Decode inputs: sequence b holds n_b keys; its query sits at n_b - 1.
+                window_only: bool = False, shuffle: bool = True, q_len: int = 1) -> DecodeCase:
+    """Decode inputs: sequence b holds n_b keys; its q_len queries sit at
+    n_b - q_len .. n_b - 1 (one query at n_b - 1 by default).
 
-    With ``window_only`` (local layers) only the pages covering the last
-    ``window`` positions hold real keys; every earlier table entry points to
-    pool page 0, which is NaN-filled and must never influence the output.
+    With ``window_only`` (local layers) only the pages covering the keys the
+    queries see (the last ``window + q_len - 1`` positions) hold real keys;
+    every earlier table entry points to pool page 0, which is NaN-filled and
+    must never influence the output.
     """
     P = spec.page_size
     B = len(seq_lens)
     g = _dev_gen(seed, device)
-    q = _randn((B, spec.num_q_heads, spec.head_dim), g, device, spec.dtype)
-    bias = _randn((B, spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
+    q = _randn((B * q_len, spec.num_q_heads, spec.head_dim), g, device, spec.dtype)
+    bias = _randn((B * q_len, spec.num_q_heads, spec.rel_extent), g, device, spec.dtype,
                   std=spec.bias_std)
 
     pages_per = [max(1, -(-n // P)) for n in seq_lens]
     first_real = []
     for n, npg in zip(seq_lens, pages_per):
         if window_only and spec.window > 0:
-            first_real.append(max(0, n - spec.window) // P)
+            first_real.append(max(0, n - q_len - spec.window + 1) // P)
         else:
             first_real.append(0)
     real_per = [npg - f for npg, f in zip(pages_per, first_real)]
@@ -405,7 +411,7 @@ def make_decode(spec: LayerSpec, seq_lens: List[int], seed: int, device="cpu",
         spec=spec, seq_lens=list(seq_lens), q=q, bias=bias,
         seq_lens_dev=torch.tensor(list(seq_lens), dtype=torch.int32, device=device),
         block_table=table.to(device), k_pool=k_pool, v_pool=v_pool, seed=seed,
-        window_only=window_only, _kv_first_page=first_real)
+        window_only=window_only, _kv_first_page=first_real, q_len=q_len)
 
 
 # ---------------------------------------------------------------------------
@@ -435,6 +441,11 @@ WORKLOADS = {
         local=LayerSpec(**LOCAL), glob=LayerSpec(**GLOBAL)),
     "long-decode-32x131072": dict(
         kind="decode", seed=1005, seq_lens=[131072] * 32, num_splits=16,
+        spec=LayerSpec(**GLOBAL)),
+    # verification of drafted tokens (multi-token prediction): 4 new tokens
+    # per sequence over the long-decode cache shape, 8 partitions of 16384 keys
+    "mtp-verify-32x131072-q4": dict(
+        kind="mtp-verify", seed=1011, seq_lens=[131072] * 32, q_len=4, num_splits=8,
         spec=LayerSpec(**GLOBAL)),
     # K/V append of a prefill chunk: 8 sequences, 2048 new tokens each onto
     # 2048 cached ones, local-layer pools
@@ -474,6 +485,9 @@ def build_workload(name: str, device="cpu"):
                                         num_pages=w["num_pages"], shuffle=w["shuffle"])}
     if w["kind"] == "decode":
         return {"decode": make_decode(w["spec"], w["seq_lens"], w["seed"], device)}
+    if w["kind"] == "mtp-verify":
+        return {"verify": make_decode(w["spec"], w["seq_lens"], w["seed"], device,
+                                      q_len=w["q_len"])}
     if w["kind"] == "append":
         return {"append": make_append(w["spec"], w["key_lens"], w["new_lens"], w["seed"], device)}
     if w["kind"] == "prefill-history":

@@ -17,7 +17,8 @@ from typing import Optional
 import torch
 
 __all__ = ["prefill", "prefill_fused", "decode", "decode_noalloc", "decode_num_splits",
-           "decode_workspace_size", "kv_append", "window_ring_pages", "ring_block_table",
+           "decode_workspace_size", "decode_multi", "decode_multi_num_splits",
+           "decode_multi_workspace_size", "kv_append", "window_ring_pages", "ring_block_table",
            "status_string", "RbaError", "library_path", "load", "DECODE_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +35,8 @@ RBA_F32 = 1
 
 # every symbol include/rba.h declares
 EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_noalloc",
-            "rba_decode_num_splits", "rba_decode_workspace_size", "rba_kv_append",
+            "rba_decode_num_splits", "rba_decode_workspace_size", "rba_decode_multi",
+            "rba_decode_multi_num_splits", "rba_decode_multi_workspace_size", "rba_kv_append",
             "rba_window_ring_pages", "rba_ring_block_table", "rba_status_string")
 
 # RBA_DECODE_SCRATCH_BYTES of include/rba.h: the workspace limit of rba_decode_noalloc
@@ -110,6 +112,17 @@ def load():
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p]
     lib.rba_decode_noalloc.restype = ctypes.c_int
+    lib.rba_decode_multi.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(rba_kv_cache),
+                                     P(rba_page_table), ctypes.c_int32, ctypes.c_void_p,
+                                     P(rba_attn_params), ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    lib.rba_decode_multi.restype = ctypes.c_int
+    for fn, res in (("rba_decode_multi_num_splits", ctypes.c_int32),
+                    ("rba_decode_multi_workspace_size", ctypes.c_size_t)):
+        getattr(lib, fn).argtypes = [ctypes.c_int32, P(rba_kv_cache), P(rba_page_table),
+                                     ctypes.c_int32, P(rba_attn_params), ctypes.c_int32]
+        getattr(lib, fn).restype = res
     lib.rba_ring_block_table.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_void_p]
     lib.rba_ring_block_table.restype = ctypes.c_int
@@ -383,4 +396,71 @@ def decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                 int(max_seq_len), _dev(bias, "bias"), ctypes.byref(prm),
                                 int(num_splits), _dev(out, "out"), lse_ptr, _stream(stream))
     _check(st, "rba_decode_noalloc")
+    return out
+
+
+def _multi_structs(q, q_len, k_pool, v_pool, block_table, seq_lens, bias, window, sm_scale):
+    if q.dim() != 3 or bias.dim() != 3 or bias.shape[:2] != q.shape[:2]:
+        raise ValueError("q must be [B*q_len,Hq,D] and bias [B*q_len,Hq,R]")
+    if q_len < 1 or q.shape[0] != block_table.shape[0] * q_len:
+        raise ValueError("q must hold q_len rows per sequence of the block table")
+    return _structs(k_pool, v_pool, block_table, seq_lens, q.shape[1], window, bias.shape[2],
+                    sm_scale)
+
+
+def decode_multi_num_splits(q, q_len, k_pool, v_pool, block_table, seq_lens, max_seq_len, bias, *,
+                            window: int, sm_scale: float, num_splits: int = 0) -> int:
+    lib = load()
+    kv, pt, prm = _multi_structs(q, q_len, k_pool, v_pool, block_table, seq_lens, bias, window,
+                                 sm_scale)
+    return int(lib.rba_decode_multi_num_splits(int(q_len), ctypes.byref(kv), ctypes.byref(pt),
+                                               int(max_seq_len), ctypes.byref(prm),
+                                               int(num_splits)))
+
+
+def decode_multi_workspace_size(q, q_len, k_pool, v_pool, block_table, seq_lens, max_seq_len,
+                                bias, *, window: int, sm_scale: float, num_splits: int = 0) -> int:
+    lib = load()
+    kv, pt, prm = _multi_structs(q, q_len, k_pool, v_pool, block_table, seq_lens, bias, window,
+                                 sm_scale)
+    return int(lib.rba_decode_multi_workspace_size(int(q_len), ctypes.byref(kv), ctypes.byref(pt),
+                                                   int(max_seq_len), ctypes.byref(prm),
+                                                   int(num_splits)))
+
+
+def decode_multi(q: torch.Tensor, q_len: int, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                 bias: torch.Tensor, *, window: int, sm_scale: float, num_splits: int = 0,
+                 workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rba_decode_multi: q [B*q_len,Hq,D], bias [B*q_len,Hq,R]; sequence b's
+    q_len tokens are its last positions.  Returns out [B*q_len,Hq,D].
+    ``workspace`` (uint8 device tensor) is allocated with torch when not
+    given and the call needs one."""
+    lib = load()
+    kv, pt, prm = _multi_structs(q, q_len, k_pool, v_pool, block_table, seq_lens, bias, window,
+                                 sm_scale)
+    if q.dtype != k_pool.dtype or bias.dtype != k_pool.dtype:
+        raise TypeError("q, bias and the pools must share one dtype")
+    need = int(lib.rba_decode_multi_workspace_size(int(q_len), ctypes.byref(kv), ctypes.byref(pt),
+                                                   int(max_seq_len), ctypes.byref(prm),
+                                                   int(num_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lse_ptr = None
+    if lse is not None:
+        if lse.shape != q.shape[:2]:
+            raise ValueError("lse must be [B*q_len, Hq]")
+        lse_ptr = _dev(lse, "lse", torch.float32)
+    st = lib.rba_decode_multi(_dev(q, "q"), int(q_len), ctypes.byref(kv), ctypes.byref(pt),
+                              int(max_seq_len), _dev(bias, "bias"), ctypes.byref(prm),
+                              int(num_splits), ws_ptr, ws_bytes, _dev(out, "out"), lse_ptr,
+                              _stream(stream))
+    _check(st, "rba_decode_multi")
     return out

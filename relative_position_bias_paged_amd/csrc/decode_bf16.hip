@@ -340,14 +340,18 @@ __global__ __launch_bounds__(64) void decode_bf16_kernel(DecodeArgs a) {
 // One wave per (sequence, query head): out = sum_j w_j o_j / sum_j w_j with
 // w_j = exp(lse_j - max_j lse_j) over the partitions that hold keys (the
 // first ceil((p_end - p_first) / chunk) of them; the others wrote nothing).
+// With q_len > 1 the row's sequence is orow / (Hq * q_len) and the
+// partitions cover the keys any of its q_len queries sees.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int bf16_out) {
   constexpr int E = D / 64;      // elements per lane
   const int lane = threadIdx.x;
   const size_t orow = blockIdx.x;
   const int S = a.num_splits;
-  const int n = a.seq_lens[orow / a.Hq];
-  const int lo = (a.window > 0) ? max(0, n - a.window) : 0;
+  const int ql = a.q_len;
+  const int n_raw = a.seq_lens[orow / ((size_t)a.Hq * ql)];
+  const int n = ql > 1 ? max(n_raw, ql) : n_raw;
+  const int lo = (a.window > 0) ? max(0, n - ql - a.window + 1) : 0;
   const int span = ((n + a.page_size - 1) >> a.log2_page) - (lo >> a.log2_page);
   const int S_b = n > 0 ? min(S, (span + a.chunk_pages - 1) / a.chunk_pages) : 0;
   const float *pl = a.part_lse + orow * S;
@@ -384,7 +388,8 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int bf16_out) {
 
 // Largest-first order of the (sequence, partition) items for the decode grid:
 // a counting sort on (chunk_pages - pages) >> plan_shift, with the empty
-// partitions last as {-1, 0}.  One work-group; positions within a bucket
+// partitions last as {-1, 0}.  (Shared with decode_multi_kernel: the record
+// carries the key count n_b it planned with.)  One work-group; positions within a bucket
 // follow LDS atomics, which changes dispatch order only, never a result.
 constexpr int kPlanBuckets = 257;        // 256 size classes + the empty ones
 __global__ __launch_bounds__(1024) void plan_kernel(DecodeArgs a) {
@@ -393,11 +398,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(DecodeArgs a) {
   const int C = a.chunk_pages;
   const int items = a.num_seqs * S;
   const int lp = a.log2_page;
+  const int ql = a.q_len;
   auto bucket_of = [&](int it, int &n) {
     const int b = it / S;
     const int j = it - b * S;
-    n = a.seq_lens[b];
-    const int lo = (a.window > 0) ? max(0, n - a.window) : 0;
+    n = ql > 1 ? max(a.seq_lens[b], ql) : a.seq_lens[b];
+    const int lo = (a.window > 0) ? max(0, n - ql - a.window + 1) : 0;
     const int p_first = lo >> lp;
     const int p_end = (n + a.page_size - 1) >> lp;
     const int pages = (n > 0) ? max(0, min(p_first + (j + 1) * C, p_end) - (p_first + j * C)) : 0;
@@ -435,6 +441,7 @@ hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s) {
+  if (a.q_len != 1 || a.hpw != 4) return hipErrorInvalidValue;
   const long long items = (long long)a.num_seqs * a.Hkv * a.num_splits * a.head_groups;
   dim3 grid((unsigned)items), block(64);
   if (head_dim == 128) {
@@ -448,7 +455,7 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s) 
 }
 
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStream_t s) {
-  dim3 grid((unsigned)((long long)a.num_seqs * a.Hq)), block(64);
+  dim3 grid((unsigned)((long long)a.num_seqs * a.q_len * a.Hq)), block(64);
   if (head_dim == 128) {
     hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, s, a, bf16_out ? 1 : 0);
   } else if (head_dim == 64) {

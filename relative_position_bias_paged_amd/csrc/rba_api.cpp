@@ -62,13 +62,14 @@ bool pool_ok(const rba_kv_cache *kv, const rba_page_table *pt) {
          pt->max_pages_per_seq > 0;
 }
 
-// Upper bound on the pages one decode row touches: the visible keys
-// [max(0, n - window), n) span at most ceil(visible / P) pages, plus one when
-// a window start falls inside a page.
-int decode_pages_max(const rba_page_table *pt, int max_seq_len, int window) {
+// Upper bound on the pages the queries of one sequence touch: with q_len
+// queries at positions n - q_len .. n - 1, the visible keys
+// [max(0, n - q_len - window + 1), n) span at most ceil(visible / P) pages,
+// plus one when a window start falls inside a page.
+int decode_pages_max(const rba_page_table *pt, int max_seq_len, int window, int q_len = 1) {
   const long long P = pt->page_size;
   long long visible = max_seq_len;
-  if (window > 0 && window < visible) visible = window;
+  if (window > 0 && (long long)window + q_len - 1 < visible) visible = (long long)window + q_len - 1;
   long long pages = (visible + P - 1) / P + (window > 0 ? 1 : 0);
   if (pages < 1) pages = 1;
   const long long cap = (max_seq_len + P - 1) / P;
@@ -81,17 +82,26 @@ struct SplitPlan {
   int chunk_pages;
 };
 
+// Query heads per decode wave: 4 for single-token decode; with q_len > 1,
+// as many as fit the 16 matrix rows of a wave with their q_len tokens each.
+int decode_heads_per_wave(int G, int q_len) {
+  if (q_len <= 1) return 4;
+  const int fit = 16 / q_len;
+  return fit < G ? fit : G;
+}
+
 SplitPlan plan_splits(const rba_kv_cache *kv, const rba_page_table *pt, int max_seq_len,
-                      const rba_attn_params *p, int num_splits) {
+                      const rba_attn_params *p, int num_splits, int q_len = 1) {
   if (kv->dtype == RBA_F32) return {1, 1 << 30};
-  const int pm = decode_pages_max(pt, max_seq_len, p->window);
+  const int pm = decode_pages_max(pt, max_seq_len, p->window, q_len);
   int s;
   if (num_splits > 0) {
     s = num_splits;
   } else {
     s = (pm + kAutoChunkPages - 1) / kAutoChunkPages;
     const int G = p->num_q_heads / kv->num_kv_heads;
-    const long long base = (long long)pt->num_seqs * kv->num_kv_heads * ((G + 3) / 4);
+    const int hpw = decode_heads_per_wave(G, q_len);
+    const long long base = (long long)pt->num_seqs * kv->num_kv_heads * ((G + hpw - 1) / hpw);
     if (base > 0 && base * s < kAutoMinWaves) s = (int)((kAutoMinWaves + base - 1) / base);
   }
   if (s > kMaxSplits) s = kMaxSplits;
@@ -112,17 +122,17 @@ struct WorkspaceLayout {
 size_t pad256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WorkspaceLayout workspace_layout(const rba_kv_cache *kv, const rba_page_table *pt,
-                                 const rba_attn_params *p, int splits) {
+                                 const rba_attn_params *p, int splits, int q_len = 1) {
   if (splits <= 1) return {0, 0, 0};
-  const size_t rows = (size_t)pt->num_seqs * p->num_q_heads;
+  const size_t rows = (size_t)pt->num_seqs * q_len * p->num_q_heads;
   const size_t lse_off = pad256(rows * splits * kv->head_dim * sizeof(float));
   const size_t plan_off = pad256(lse_off + rows * splits * sizeof(float));
   return {lse_off, plan_off, plan_off + (size_t)pt->num_seqs * splits * 2 * sizeof(int32_t)};
 }
 
 size_t workspace_bytes_for(const rba_kv_cache *kv, const rba_page_table *pt,
-                           const rba_attn_params *p, int splits) {
-  return workspace_layout(kv, pt, p, splits).bytes;
+                           const rba_attn_params *p, int splits, int q_len = 1) {
+  return workspace_layout(kv, pt, p, splits, q_len).bytes;
 }
 
 }  // namespace
@@ -308,11 +318,13 @@ namespace {
 // plan and *need the workspace bytes it takes (0 without partitions).
 rba_status decode_check(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
                         int32_t max_seq_len, const void *bias, const rba_attn_params *params,
-                        int32_t num_splits, void *out, float *lse, SplitPlan *sp, size_t *need) {
+                        int32_t num_splits, void *out, float *lse, SplitPlan *sp, size_t *need,
+                        int q_len = 1) {
   rba_status st = check_layer(kv, pt, params);
   if (st != RBA_OK) return st;
-  if (max_seq_len < 0 || num_splits < 0) return RBA_ERR_INVALID_ARG;
-  *sp = plan_splits(kv, pt, max_seq_len, params, num_splits);
+  if (max_seq_len < 0 || num_splits < 0 || q_len < 1) return RBA_ERR_INVALID_ARG;
+  if (q_len > 16 || (q_len > 1 && kv->dtype != RBA_BF16)) return RBA_ERR_UNSUPPORTED;
+  *sp = plan_splits(kv, pt, max_seq_len, params, num_splits, q_len);
   *need = 0;
   if (pt->num_seqs == 0) return RBA_OK;
   if (q == nullptr || bias == nullptr || out == nullptr || pt->seq_lens == nullptr)
@@ -322,7 +334,11 @@ rba_status decode_check(const void *q, const rba_kv_cache *kv, const rba_page_ta
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
   if ((long long)max_seq_len > (long long)pt->max_pages_per_seq * pt->page_size)
     return RBA_ERR_INVALID_ARG;
-  *need = workspace_bytes_for(kv, pt, params, sp->splits);
+  // every sequence holds its q_len new tokens' keys: the kernels read a
+  // shorter length as q_len, which max_seq_len (and the table) must cover
+  if (q_len > 1 && max_seq_len < q_len) return RBA_ERR_INVALID_ARG;
+  if ((long long)pt->num_seqs * q_len * params->num_q_heads > 0x7fffffffLL) return RBA_ERR_UNSUPPORTED;
+  *need = workspace_bytes_for(kv, pt, params, sp->splits, q_len);
   return RBA_OK;
 }
 
@@ -330,7 +346,7 @@ rba_status decode_check(const void *q, const rba_kv_cache *kv, const rba_page_ta
 rba_status decode_launch(const void *q, const rba_kv_cache *kv, const rba_page_table *pt,
                          const void *bias, const rba_attn_params *params, const SplitPlan &sp,
                          size_t need, void *workspace, void *out, float *lse,
-                         hipStream_t stream) {
+                         hipStream_t stream, int q_len = 1) {
   rba::DecodeArgs a{};
   a.q = q;
   a.k_pool = kv->k_pool;
@@ -352,9 +368,11 @@ rba_status decode_launch(const void *q, const rba_kv_cache *kv, const rba_page_t
   a.sm_scale = params->sm_scale;
   a.num_splits = sp.splits;
   a.chunk_pages = sp.chunk_pages;
-  a.head_groups = (a.G + 3) / 4;
+  a.q_len = q_len;
+  a.hpw = decode_heads_per_wave(a.G, q_len);
+  a.head_groups = (a.G + a.hpw - 1) / a.hpw;
   if (need > 0) {
-    const WorkspaceLayout wl = workspace_layout(kv, pt, params, sp.splits);
+    const WorkspaceLayout wl = workspace_layout(kv, pt, params, sp.splits, q_len);
     char *base = static_cast<char *>(workspace);
     a.part_o = reinterpret_cast<float *>(base);
     a.part_lse = reinterpret_cast<float *>(base + wl.lse_off);
@@ -376,7 +394,8 @@ rba_status decode_launch(const void *q, const rba_kv_cache *kv, const rba_page_t
       err = rba::launch_decode_plan(a, stream);
       if (err != hipSuccess) return RBA_ERR_HIP;
     }
-    err = rba::launch_decode_bf16(a, kv->head_dim, stream);
+    err = q_len > 1 ? rba::launch_decode_multi(a, kv->head_dim, stream)
+                    : rba::launch_decode_bf16(a, kv->head_dim, stream);
     if (err == hipSuccess && sp.splits > 1) err = rba::launch_merge(a, kv->head_dim, true, stream);
   }
   return err == hipSuccess ? RBA_OK : RBA_ERR_HIP;
@@ -445,4 +464,43 @@ RBA_EXPORT rba_status rba_decode_noalloc(const void *q, const rba_kv_cache *kv,
   void *ws = nullptr;
   if (need > 0 && scratch_for_current_device(&ws) != hipSuccess) return RBA_ERR_HIP;
   return decode_launch(q, kv, pt, bias, params, sp, need, ws, out, lse, stream);
+}
+
+RBA_EXPORT int32_t rba_decode_multi_num_splits(int32_t q_len, const rba_kv_cache *kv,
+                                               const rba_page_table *pt, int32_t max_seq_len,
+                                               const rba_attn_params *params, int32_t num_splits) {
+  if (check_layer(kv, pt, params) != RBA_OK || max_seq_len < 0 || num_splits < 0 || q_len < 1 ||
+      q_len > 16)
+    return 0;
+  return plan_splits(kv, pt, max_seq_len, params, num_splits, q_len).splits;
+}
+
+RBA_EXPORT size_t rba_decode_multi_workspace_size(int32_t q_len, const rba_kv_cache *kv,
+                                                  const rba_page_table *pt, int32_t max_seq_len,
+                                                  const rba_attn_params *params,
+                                                  int32_t num_splits) {
+  if (check_layer(kv, pt, params) != RBA_OK || max_seq_len < 0 || num_splits < 0 || q_len < 1 ||
+      q_len > 16)
+    return 0;
+  const SplitPlan sp = plan_splits(kv, pt, max_seq_len, params, num_splits, q_len);
+  return workspace_bytes_for(kv, pt, params, sp.splits, q_len);
+}
+
+RBA_EXPORT rba_status rba_decode_multi(const void *q, int32_t q_len, const rba_kv_cache *kv,
+                                       const rba_page_table *pt, int32_t max_seq_len,
+                                       const void *bias, const rba_attn_params *params,
+                                       int32_t num_splits, void *workspace,
+                                       size_t workspace_bytes, void *out, float *lse,
+                                       hipStream_t stream) {
+  SplitPlan sp;
+  size_t need;
+  const rba_status st = decode_check(q, kv, pt, max_seq_len, bias, params, num_splits, out, lse,
+                                     &sp, &need, q_len);
+  if (st != RBA_OK || pt->num_seqs == 0) return st;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return RBA_ERR_WORKSPACE;
+  }
+  return decode_launch(q, kv, pt, bias, params, sp, need, workspace, out, lse, stream, q_len);
 }

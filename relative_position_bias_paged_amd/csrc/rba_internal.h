@@ -52,7 +52,13 @@ struct DecodeArgs {
   int32_t window, R;
   int32_t num_splits;        // S
   int32_t chunk_pages;       // pages per partition
-  int32_t head_groups;       // ceil(G / 4): query-head groups per KV head
+  int32_t head_groups;       // query-head groups per KV head: ceil(G / hpw)
+  int32_t hpw;               // query heads per wave (decode_bf16_kernel: 4)
+  // Query tokens per sequence: 1 for single-token decode.  With q_len > 1
+  // (decode_multi_kernel) q, bias and out hold q_len rows per sequence,
+  // row b * q_len + i at position n_b - q_len + i, n_b = max(seq_lens[b],
+  // q_len); part_o is then [B * q_len][Hq][S][D], part_lse [B * q_len][Hq][S].
+  int32_t q_len;
   float sm_scale;
 };
 
@@ -77,5 +83,6 @@ hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStr
 hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_decode_multi(const DecodeArgs &a, int head_dim, hipStream_t s);
 
 }  // namespace rba

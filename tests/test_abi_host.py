@@ -317,6 +317,67 @@ def test_scratch_limit_matches_header():
     assert m and int(m.group(1)) << int(m.group(2)) == rba.DECODE_SCRATCH_BYTES
 
 
+def _decode_multi(kv, pt, prm, q=FAKE, q_len=4, max_len=1000, bias=FAKE, splits=0, ws=None,
+                  ws_bytes=0, out=FAKE, lse=None):
+    return rba.load().rba_decode_multi(q, q_len, ctypes.byref(kv), ctypes.byref(pt), max_len,
+                                       bias, ctypes.byref(prm), splits, ws, ws_bytes, out, lse,
+                                       None)
+
+
+@pytest.mark.parametrize("kwargs,expected", [
+    (dict(q=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(bias=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(out=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(q_len=0), rba.RBA_ERR_INVALID_ARG),
+    (dict(q_len=-2), rba.RBA_ERR_INVALID_ARG),
+    (dict(q_len=17), rba.RBA_ERR_UNSUPPORTED),
+    (dict(max_len=3), rba.RBA_ERR_INVALID_ARG),          # shorter than the new tokens
+    (dict(max_len=256 * 64 + 1), rba.RBA_ERR_INVALID_ARG),
+    (dict(splits=-1), rba.RBA_ERR_INVALID_ARG),
+])
+def test_decode_multi_argument_errors(kwargs, expected):
+    kv, pt, prm = _layer()
+    assert _decode_multi(kv, pt, prm, **kwargs) == expected
+
+
+def test_decode_multi_layer_checks_and_dtype():
+    kv, pt, prm = _layer(hq=30, hkv=8)
+    assert _decode_multi(kv, pt, prm) == rba.RBA_ERR_INVALID_ARG
+    kv, pt, prm = _layer(dtype=rba.RBA_F32)
+    assert _decode_multi(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED   # fp32: prefill over history
+    kv, pt, prm = _layer(seqs=0)
+    assert _decode_multi(kv, pt, prm, q=0, bias=0, out=0) == rba.RBA_OK
+
+
+def test_decode_multi_plan_and_workspace():
+    lib = rba.load()
+
+    def plan(q_len, max_len, splits, **kw):
+        kv, pt, prm = _layer(**kw)
+        n = lib.rba_decode_multi_num_splits(q_len, ctypes.byref(kv), ctypes.byref(pt), max_len,
+                                            ctypes.byref(prm), splits)
+        ws = lib.rba_decode_multi_workspace_size(q_len, ctypes.byref(kv), ctypes.byref(pt),
+                                                 max_len, ctypes.byref(prm), splits)
+        return n, ws
+
+    # 32 sequences of 131072 keys, 4 new tokens each, 8 partitions: partials
+    # and LSE for 32*4*32 rows, then the (sequence, partition) plan
+    n, ws = plan(4, 131072, 8, seqs=32, max_pages=2048, pages=65536)
+    rows = 32 * 4 * 32
+    assert n == 8
+    assert ws == rows * 8 * 128 * 4 + rows * 8 * 4 + 32 * 8 * 8
+    # q_len 1 plans like rba_decode
+    kv, pt, prm = _layer(seqs=32, max_pages=2048, pages=65536)
+    one = lib.rba_decode_workspace_size(ctypes.byref(kv), ctypes.byref(pt), 131072,
+                                        ctypes.byref(prm), 16)
+    assert plan(1, 131072, 16, seqs=32, max_pages=2048, pages=65536) == (16, one)
+    # a local layer's queries see window + q_len - 1 keys: at most 10 pages of 64
+    n, _ = plan(8, 32768, 64, seqs=4, hkv=16, W=512, R=512, max_pages=512, pages=3000)
+    assert n == 10
+    assert plan(4, 1000, 0, hq=31) == (0, 0)
+    assert plan(17, 1000, 0) == (0, 0)
+
+
 def test_status_strings():
     for code, name in [(0, "RBA_OK"), (1, "RBA_ERR_INVALID_ARG"), (2, "RBA_ERR_UNSUPPORTED"),
                        (3, "RBA_ERR_WORKSPACE"), (4, "RBA_ERR_HIP")]:
