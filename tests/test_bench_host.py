@@ -41,8 +41,9 @@ def _fake_torch(log):
 
 def test_time_steps_brackets_exactly_the_timed_steps():
     log = []
-    wall, ev = bench.time_steps(lambda: log.append("step"), steps=7, warmup=3,
-                                torch=_fake_torch(log))
+    wall, ev, warm_steps, warm_ms = bench.time_steps(lambda: log.append("step"), steps=7,
+                                                     warmup=3, torch=_fake_torch(log))
+    assert warm_steps == 3 and warm_ms >= 0.0
     assert log.count("step") == 10
     assert log.count("event") == 2
     first = log.index("event")
@@ -60,7 +61,30 @@ def test_time_steps_warms_for_the_minimum_time():
         log.append("step")
         time.sleep(0.002)
 
-    bench.time_steps(step, steps=2, warmup=2, torch=_fake_torch(log), min_warm_ms=30.0)
+    _, _, warm_steps, warm_ms = bench.time_steps(step, steps=2, warmup=2, torch=_fake_torch(log),
+                                                 min_warm_ms=30.0)
     first = log.index("event")
     assert log[:first].count("step") >= 15       # at least 30 ms of 2 ms steps
+    assert warm_steps == log[:first].count("step") and warm_ms >= 30.0
     assert log[first:].count("step") == 2
+
+
+def test_decode_work_counts_each_key_once():
+    """Algorithmic bytes of a multi-token decode: the K/V of the keys any of
+    a sequence's queries sees, once, plus q/out and the bias entries used."""
+    import types as _t
+    sp = _t.SimpleNamespace(head_dim=128, num_q_heads=32, num_kv_heads=8, window=0,
+                            rel_extent=1024)
+    one = _t.SimpleNamespace(spec=sp, seq_lens=[5000], q_len=1)
+    four = _t.SimpleNamespace(spec=sp, seq_lens=[5000], q_len=4)
+    f1, b1 = bench.decode_work(one)
+    f4, b4 = bench.decode_work(four)
+    kv = 5000 * 8 * 128 * 2 * 2
+    assert b1 == kv + 32 * 1024 * 2 + 32 * 128 * 2 * 2
+    assert b4 == kv + 4 * 32 * 1024 * 2 + 4 * 32 * 128 * 2 * 2
+    assert f4 == 4 * 128 * 32 * (4997 + 4998 + 4999 + 5000)
+    loc = _t.SimpleNamespace(head_dim=128, num_q_heads=32, num_kv_heads=16, window=512,
+                             rel_extent=512)
+    f, b = bench.decode_work(_t.SimpleNamespace(spec=loc, seq_lens=[5000], q_len=4))
+    assert b == (512 + 3) * 16 * 128 * 2 * 2 + 4 * 32 * 512 * 2 + 4 * 32 * 128 * 2 * 2
+    assert f == 4 * 128 * 32 * 512 * 4
