@@ -516,8 +516,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int vsw = v_swizzle<D>(vrow);                   // rows ks*16+vrow(+4) share it
   const int vbase = vrow * D + (vi & 1) * 4;
 
-  auto compute_tile = [&](int s0, const uint16_t *kl, const uint16_t *vl, const u32x4_t (&bp)[4]) {
-    const bool fixed0 = in_range(s0, p0_lo, p0_span);   // clamp-only, unmasked
+  // fixed_tag: std::integral_constant<bool, true> on tiles known (for the
+  // whole work-group) to be clamp-only and unmasked, which then compile to
+  // score path 0 with no classification, bias or mask code at all.
+  auto compute_tile = [&](auto fixed_tag, int s0, const uint16_t *kl, const uint16_t *vl,
+                          const u32x4_t (&bp)[4]) {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
+    const bool fixed0 = FIXED || in_range(s0, p0_lo, p0_span);   // clamp-only, unmasked
     if (!fixed0 && !in_range(s0, act_lo, act_span)) return;   // no key of the tile is visible
     const bool need_mask = s0 > s_diag || s0 <= s_wedge || s0 > s_tail;
     const bool band = s0 > s_band;
@@ -711,11 +716,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // (Fused variant: the bias product of tile s_cur goes into the stage first,
   // from the W^T buffer loaded with the tile; the W^T rows of s_nxt load with
   // its K/V into the other buffer.)
-  auto step = [&](uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn, const uint16_t *wc,
-                  uint16_t *wn, int &page_nxt) {
+  auto step = [&](auto fixed_tag, uint16_t *kc, uint16_t *vc, uint16_t *kn, uint16_t *vn,
+                  const uint16_t *wc, uint16_t *wn, int &page_nxt) {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
     const int s0 = s_cur;
     const bool more = --steps_left > 0;
-    if (wave_band(s0)) {
+    if (!FIXED && wave_band(s0)) {
       fuse_bias(wc);
       load_bias(s0, bias_r);
     }
@@ -730,7 +736,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         stage_bias(s_nxt);
       }
     }
-    compute_tile(s0, kc, vc, bias_r);
+    compute_tile(fixed_tag, s0, kc, vc, bias_r);
     __syncthreads();
     s_cur = s_nxt;
     s_nxt = s_nxt2;
@@ -747,9 +753,32 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   int page_nxt = tile_page(s_nxt);
   __syncthreads();
 
-  for (;;) {
-    if (!step(k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt)) break;
-    if (!step(k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt)) break;
+  // Global layers visit their tiles in natural order from 0, and the leading
+  // ones, up to the last tile at distance >= R-1 from the work-group's first
+  // query (and before the sequence's last tile), are clamp-only and
+  // unmasked for every wave: they run a loop of their own with the score
+  // path fixed at compile time.  The diagonal tile is never among them, so
+  // the general loop always follows.
+  typedef std::integral_constant<bool, true> FixedTile;
+  typedef std::integral_constant<bool, false> AnyTile;
+  int n_fixed = 0;
+  if (W <= 0) {
+    const int lim = min(P0 - (BN - 2) - R, n_k - BN);
+    n_fixed = lim < 0 ? 0 : min(lim / BN + 1, n_t - 1);
+  }
+  int i_fixed = 0;
+  for (; i_fixed + 2 <= n_fixed; i_fixed += 2) {
+    step(FixedTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt);
+    step(FixedTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
+  }
+  bool go = true;
+  if (i_fixed < n_fixed) {   // an odd count: the general loop starts on buffer 1
+    step(FixedTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt);
+    go = step(AnyTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
+  }
+  while (go) {
+    if (!step(AnyTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt)) break;
+    if (!step(AnyTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt)) break;
   }
 
   // ---- epilogue ------------------------------------------------------------
