@@ -24,7 +24,7 @@ namespace {
 #ifndef RBA_PREFILL_WAVES_GLOBAL
 #define RBA_PREFILL_WAVES_GLOBAL 8
 #endif
-constexpr int kF32Rows = 64;         // queries per fp32 prefill work-group
+constexpr int kF32Rows = 4;          // queries (one wave each) per fp32 prefill work-group
 constexpr int kMaxSplits = 256;
 constexpr int kAutoChunkPages = 64;  // automatic partitions hold about this many pages
 constexpr long long kAutoMinWaves = 2048;
