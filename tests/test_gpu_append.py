@@ -215,3 +215,86 @@ def test_graph_captured_decode_step(W, R):
                             ri._cumsum(lens_now), window=W, rel_extent=R, sm_scale=scale)
         assert_parity(gb["out"], ref, torch.bfloat16, f"graph step {s}")
     assert torch.equal(k_pool.view(torch.int16), k_eager.view(torch.int16))
+
+
+def test_graph_captured_mtp_verify_step():
+    """Multi-token verification step (append the 4 drafted tokens' K/V, then
+    rba_decode_multi over the whole cache) captured once in a HIP graph and
+    replayed for three steps with new inputs copied into its buffers: every
+    replay equals the eager step bit for bit and matches the oracle's
+    prefill over the history."""
+    dev = device()
+    dtype, Hq, Hkv, D, P, R, W, L = torch.bfloat16, 8, 2, 128, 64, 256, 0, 4
+    scale = D ** -0.5
+    lens0 = [100, 1900, 64, 511]
+    steps = 3
+    B = len(lens0)
+    cap = [n + L * steps for n in lens0]
+    max_len = max(cap)
+    k_pool, v_pool, table = _pool_case(dev, dtype, Hkv, D, P, cap, seed=81)
+    tab, kc, vc = table.cpu(), k_pool.cpu(), v_pool.cpu()
+    k_log = [[kc[int(tab[b, s // P]), :, s % P, :] for s in range(n)] for b, n in enumerate(lens0)]
+    v_log = [[vc[int(tab[b, s // P]), :, s % P, :] for s in range(n)] for b, n in enumerate(lens0)]
+    gen = torch.Generator(device="cpu").manual_seed(83)
+    step_in = []
+    for s in range(steps):
+        step_in.append(dict(
+            q=torch.randn((B * L, Hq, D), generator=gen).to(dtype),
+            bias=torch.randn((B * L, Hq, R), generator=gen).to(dtype),
+            k=torch.randn((B * L, Hkv, D), generator=gen).to(dtype),
+            v=torch.randn((B * L, Hkv, D), generator=gen).to(dtype),
+            lens=torch.tensor([n + L * (s + 1) for n in lens0], dtype=torch.int32)))
+
+    def buffers():
+        return dict(q=torch.empty((B * L, Hq, D), dtype=dtype, device=dev),
+                    bias=torch.empty((B * L, Hq, R), dtype=dtype, device=dev),
+                    k=torch.empty((B * L, Hkv, D), dtype=dtype, device=dev),
+                    v=torch.empty((B * L, Hkv, D), dtype=dtype, device=dev),
+                    lens=torch.empty((B,), dtype=torch.int32, device=dev),
+                    out=torch.empty((B * L, Hq, D), dtype=dtype, device=dev))
+
+    cu = torch.arange(0, B * L + 1, L, dtype=torch.int32, device=dev)
+    gb = buffers()
+    for name in ("q", "bias", "lens"):
+        gb[name].copy_(step_in[0][name])
+    need = rba.decode_multi_workspace_size(gb["q"], L, k_pool, v_pool, table, gb["lens"], max_len,
+                                           gb["bias"], window=W, sm_scale=scale, num_splits=4)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    k_eager, v_eager = k_pool.clone(), v_pool.clone()
+
+    def step(buf, kp, vp):
+        rba.kv_append(buf["k"], buf["v"], cu, kp, vp, table, buf["lens"])
+        rba.decode_multi(buf["q"], L, kp, vp, table, buf["lens"], max_len, buf["bias"], window=W,
+                         sm_scale=scale, num_splits=4, workspace=ws, out=buf["out"])
+
+    warm = buffers()
+    for name in ("q", "bias", "k", "v", "lens"):
+        warm[name].copy_(step_in[0][name])
+    step(warm, k_pool.clone(), v_pool.clone())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(gb, k_pool, v_pool)
+    eb = buffers()
+    for s in range(steps):
+        for name in ("q", "bias", "k", "v", "lens"):
+            gb[name].copy_(step_in[s][name])
+            eb[name].copy_(step_in[s][name])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(eb, k_eager, v_eager)
+        torch.cuda.synchronize()
+        assert torch.equal(gb["out"].view(torch.int16), eb["out"].view(torch.int16)), s
+        for b in range(B):
+            for i in range(L):
+                k_log[b].append(step_in[s]["k"][b * L + i])
+                v_log[b].append(step_in[s]["v"][b * L + i])
+        lens_now = [n + L * (s + 1) for n in lens0]
+        k_all = torch.cat([torch.stack(k_log[b]) for b in range(B)])
+        v_all = torch.cat([torch.stack(v_log[b]) for b in range(B)])
+        ref = oracle.prefill_history(step_in[s]["q"], k_all, v_all, step_in[s]["bias"],
+                                     list(range(0, B * L + 1, L)), ri._cumsum(lens_now), window=W,
+                                     rel_extent=R, sm_scale=scale)
+        assert_parity(gb["out"], ref, torch.bfloat16, f"graph mtp step {s}")
+    assert torch.equal(k_pool.view(torch.int16), k_eager.view(torch.int16))

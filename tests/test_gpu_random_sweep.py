@@ -124,3 +124,39 @@ def test_random_prefill_fused(i, seed):
     assert_parity(out, ref, sp.dtype, what)
     if ref_lse.size:
         assert np.max(np.abs(lse.cpu().double().numpy() - ref_lse)) <= LSE_MAX_ABS, what
+
+
+@pytest.mark.parametrize("i,seed", _cases("decode-multi", 12))
+def test_random_decode_multi(i, seed):
+    """rba_decode_multi on random shapes: q_len 2..16, window-only pools,
+    forced partition counts; checked against the oracle's prefill over each
+    sequence's history."""
+    import oracle
+    import relative_position_bias_paged_amd as rba
+    rng = random.Random(seed)
+    sp = _random_spec(rng)
+    q_len = rng.choice([2, 3, 4, 5, 8, 16])
+    lens = [rng.choice([q_len, q_len + 1, 63, 64, 65, 300, 1000, 2500])
+            for _ in range(rng.randint(1, 5))]
+    lens = [max(n, q_len) for n in lens]
+    window_only = sp.window > 0 and rng.random() < 0.5
+    case = ri.make_decode(sp, lens, seed=seed % 100000, device=device(),
+                          window_only=window_only, q_len=q_len)
+    splits = rng.choice([0, 0, 1, 3, 16])
+    lse = torch.empty(case.q.shape[:2], dtype=torch.float32, device=case.q.device)
+    out = rba.decode_multi(case.q, q_len, case.k_pool, case.v_pool, case.block_table,
+                           case.seq_lens_dev, case.max_seq_len, case.bias, window=sp.window,
+                           sm_scale=sp.scale(), num_splits=splits, lse=lse)
+    torch.cuda.synchronize()
+    refs, ref_lses = [], []
+    for b, n in enumerate(lens):
+        k, v = case.logical_kv(b)
+        o, l = oracle.prefill_history(case.q[b * q_len:(b + 1) * q_len], k, v,
+                                      case.bias[b * q_len:(b + 1) * q_len], [0, q_len], [0, n],
+                                      window=sp.window, rel_extent=sp.rel_extent,
+                                      sm_scale=sp.scale(), want_lse=True)
+        refs.append(o)
+        ref_lses.append(l)
+    what = f"decode_multi #{i} {sp} q_len={q_len} lens={lens} splits={splits}"
+    assert_parity(out, np.concatenate(refs), sp.dtype, what)
+    assert np.max(np.abs(lse.cpu().double().numpy() - np.concatenate(ref_lses))) <= LSE_MAX_ABS, what
