@@ -151,12 +151,15 @@ def source_hash(*names):
 
 
 def _recorded(path, workload, kernel_source, key):
+    """kernel_source: one source file, or a tuple of the sources whose
+    kernels a step launches."""
     path = os.path.join(ROOT, "profiles", path)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("source_sha256") != source_hash(kernel_source):
+    sources = kernel_source if isinstance(kernel_source, tuple) else (kernel_source,)
+    if not rec or rec.get("source_sha256") != source_hash(*sources):
         return None
     return rec.get(key)
 
@@ -477,8 +480,8 @@ def line(name, args, torch, rba, ri, oracle_budget):
                                  c.max_seq_len, c.bias, window=sp.window, sm_scale=sp.scale(),
                                  num_splits=w.get("num_splits", 0), workspace=ws,
                                  out=outs["verify"])
-            kernel = "decode_multi_kernel<128> (+ merge_kernel<128>)"
-            src = "decode_multi.hip"
+            kernel = "decode_multi_kernel<128> (+ plan_kernel, merge_kernel<128>)"
+            src = ("decode_multi.hip", "decode_bf16.hip")
             splits = {"verify": rba.decode_multi_num_splits(
                 c.q, c.q_len, c.k_pool, c.v_pool, c.block_table, c.seq_lens_dev, c.max_seq_len,
                 c.bias, window=sp.window, sm_scale=sp.scale(), num_splits=w.get("num_splits", 0))}
