@@ -421,7 +421,7 @@ def line(name, args, torch, rba, ri, oracle_budget):
             ok &= bool(torch.equal(c.v_pool[pages, :, pos % P], c.v_new[cu[b]:cu[b + 1]]))
         res.update(metric="K/V append GB/s", value=round(gbs, 1), unit="GB/s",
                    ms_per_step=round(wall, 4), warmup_steps=wsteps, warmup_ms=round(wms, 1),
-                   roofline=_roofline(0, byt, ev, name, "kv_append.hip", "kv_append_kernel",
+                   roofline=_roofline(0, byt, ev, name, "kv_append.hip", "kv_append_kernel<false>",
                                       force="hbm"),
                    parity={"bit_exact": ok, "rows": int(c.k_new.shape[0]),
                            "check": "every appended row read back through the page table"},

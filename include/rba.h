@@ -341,6 +341,34 @@ rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu
                          const rba_page_table *pt, hipStream_t stream);
 
 /*
+ * The reverse of rba_kv_append: reads the K and V rows of given positions
+ * back out of the pool pages.  Row i of sequence b (cu_rows[b] <= i <
+ * cu_rows[b+1], L_b = cu_rows[b+1] - cu_rows[b] rows) is position
+ * n_b - L_b + (i - cu_rows[b]) with n_b = pt->seq_lens[b], read from pool
+ * page block_table[b * max_pages_per_seq + pos / page_size], slot
+ * pos % page_size: the slots rba_kv_append writes for the same arguments
+ * (the positional page table of the TensorRT-LLM PR #17860 page).  With
+ * cu_rows the prefix sums of seq_lens it de-pages every sequence whole, into
+ * the logical [sum n_b][num_kv_heads][head_dim] layout: a check of the
+ * page-table addressing, and an export path for a cache.
+ *
+ *  k_out, v_out  [total_rows][num_kv_heads][head_dim], the pool dtype,
+ *                16-byte aligned, written
+ *  cu_rows       device int32 [num_seqs + 1], non-decreasing, cu[0] = 0,
+ *                cu[num_seqs] = total_rows
+ *  pt->seq_lens  device, required; n_b >= L_b.  A position past
+ *                max_pages_per_seq * page_size, or a table entry outside
+ *                [0, num_pages), leaves that row of k_out and v_out
+ *                unwritten.
+ *
+ * Nothing is allocated and no device data is read on the host.  Errors as
+ * for rba_kv_append; total_rows == 0 or num_seqs == 0 is a no-op returning
+ * RBA_OK.
+ */
+rba_status rba_kv_gather(void *k_out, void *v_out, const int32_t *cu_rows, int32_t total_rows,
+                         const rba_kv_cache *kv, const rba_page_table *pt, hipStream_t stream);
+
+/*
  * Pages per sequence of a window-only pool for a layer with the given
  * window: a call that appends or queries at most max_new positions of a
  * sequence reads keys from at most window + max_new - 1 consecutive

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["prefill", "prefill_fused", "decode", "decode_noalloc", "decode_num_splits",
            "decode_workspace_size", "decode_multi", "decode_multi_num_splits",
-           "decode_multi_workspace_size", "kv_append", "window_ring_pages", "ring_block_table",
+           "decode_multi_workspace_size", "kv_append", "kv_gather", "window_ring_pages", "ring_block_table",
            "status_string", "RbaError", "library_path", "load", "DECODE_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +37,7 @@ RBA_F32 = 1
 EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_noalloc",
             "rba_decode_num_splits", "rba_decode_workspace_size", "rba_decode_multi",
             "rba_decode_multi_num_splits", "rba_decode_multi_workspace_size", "rba_kv_append",
-            "rba_window_ring_pages", "rba_ring_block_table", "rba_status_string")
+            "rba_kv_gather", "rba_window_ring_pages", "rba_ring_block_table", "rba_status_string")
 
 # RBA_DECODE_SCRATCH_BYTES of include/rba.h: the workspace limit of rba_decode_noalloc
 DECODE_SCRATCH_BYTES = 64 << 20
@@ -135,6 +135,8 @@ def load():
     lib.rba_kv_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                   P(rba_kv_cache), P(rba_page_table), ctypes.c_void_p]
     lib.rba_kv_append.restype = ctypes.c_int
+    lib.rba_kv_gather.argtypes = lib.rba_kv_append.argtypes
+    lib.rba_kv_gather.restype = ctypes.c_int
     lib.rba_window_ring_pages.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.rba_window_ring_pages.restype = ctypes.c_int32
     lib.rba_status_string.argtypes = [ctypes.c_int]
@@ -291,6 +293,35 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, cu_new: torch.Tensor,
                            _dev(cu_new, "cu_new", torch.int32), int(k_new.shape[0]),
                            ctypes.byref(kv), ctypes.byref(pt), _stream(stream))
     _check(st, "rba_kv_append")
+
+
+def kv_gather(cu_rows: torch.Tensor, total_rows: int, k_pool: torch.Tensor, v_pool: torch.Tensor,
+              block_table: torch.Tensor, seq_lens: torch.Tensor, *, k_out=None, v_out=None,
+              stream=None):
+    """rba_kv_gather: the K/V rows of positions n_b - L_b .. n_b - 1 of each
+    sequence (L_b rows per cu_rows), read out of the pool pages into
+    [total_rows, Hkv, D] tensors, which are returned (allocated unless
+    given).  cu_rows = prefix sums of seq_lens de-pages every sequence."""
+    lib = load()
+    if cu_rows.numel() != block_table.shape[0] + 1:
+        raise ValueError("cu_rows must have num_seqs + 1 entries")
+    if seq_lens is None:
+        raise ValueError("seq_lens is required")
+    shape = (int(total_rows), k_pool.shape[1], k_pool.shape[3])
+    if k_out is None:
+        k_out = torch.empty(shape, dtype=k_pool.dtype, device=k_pool.device)
+    if v_out is None:
+        v_out = torch.empty(shape, dtype=v_pool.dtype, device=v_pool.device)
+    if tuple(k_out.shape) != shape or tuple(v_out.shape) != shape:
+        raise ValueError(f"k_out and v_out must both be {list(shape)}")
+    if k_out.dtype != k_pool.dtype or v_out.dtype != k_pool.dtype:
+        raise TypeError("outputs and the pools must share one dtype")
+    kv, pt, _ = _structs(k_pool, v_pool, block_table, seq_lens, k_pool.shape[1], 0, 1, 1.0)
+    st = lib.rba_kv_gather(_dev(k_out, "k_out"), _dev(v_out, "v_out"),
+                           _dev(cu_rows, "cu_rows", torch.int32), int(total_rows),
+                           ctypes.byref(kv), ctypes.byref(pt), _stream(stream))
+    _check(st, "rba_kv_gather")
+    return k_out, v_out
 
 
 def window_ring_pages(window: int, page_size: int, max_new: int = 1) -> int:

@@ -1,10 +1,12 @@
 // kv_append.hip -- write the keys and values of new tokens into their pool
-// pages.  Sequence b holds seq_lens[b] keys after the call, its L_b new
-// tokens being the last L_b positions, so new token i of sequence b goes to
-// position seq_lens[b] - L_b + i: pool page table[b][pos / page_size], slot
-// pos % page_size (the page-table addressing of the TensorRT-LLM PR #17860
-// page, the commit that borrows the framework page table: positional
-// entries, bounded by the sequence length).
+// pages, and the reverse gather.  Sequence b holds seq_lens[b] keys after the
+// call, its L_b new tokens being the last L_b positions, so new token i of
+// sequence b goes to position seq_lens[b] - L_b + i: pool page
+// table[b][pos / page_size], slot pos % page_size (the page-table addressing
+// of the TensorRT-LLM PR #17860 page, the commit that borrows the framework
+// page table: positional entries, bounded by the sequence length).  The
+// gather reads the same slots back into token rows, through the same
+// indexing, so a gather of whole sequences de-pages the cache.
 //
 // One thread per 16-byte chunk of a new token's row, for a group of two KV
 // heads: the sequence lookup and the page read serve both rows, and all four
@@ -25,7 +27,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kHeadGroup = 2;
 
 // Block: 256 threads = (256 / chunks) tokens x chunks 16-byte chunks; grid.y
-// runs over the head groups.
+// runs over the head groups.  GATHER reverses the copy: pool slots to rows.
+template <bool GATHER>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a, int log2_chunks) {
   const int c = threadIdx.x & ((1 << log2_chunks) - 1);
   const int tok = blockIdx.x * (256 >> log2_chunks) + (threadIdx.x >> log2_chunks);
@@ -49,29 +52,45 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a, int log2_c
   const size_t src = ((size_t)tok * a.Hkv + h0) * rb + c * 16;
   const size_t dst = (((size_t)page * a.Hkv + h0) * a.page_size + (pos & (a.page_size - 1))) * rb +
                      c * 16;
+  const size_t row_step = rb;                             // next head, same token
   const size_t head_step = (size_t)a.page_size * rb;     // next head, same slot
-  const char *ks = static_cast<const char *>(a.k_new) + src;
-  const char *vs = static_cast<const char *>(a.v_new) + src;
-  char *kd = static_cast<char *>(a.k_pool) + dst;
-  char *vd = static_cast<char *>(a.v_pool) + dst;
+  char *kr = static_cast<char *>(a.k_rows) + src;
+  char *vr = static_cast<char *>(a.v_rows) + src;
+  char *kp = static_cast<char *>(a.k_pool) + dst;
+  char *vp = static_cast<char *>(a.v_pool) + dst;
   u32x4_t kv[kHeadGroup], vv[kHeadGroup];
+  if constexpr (GATHER) {
 #pragma unroll
-  for (int j = 0; j < kHeadGroup; ++j)
-    if (j < nh) {
-      kv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(ks + j * rb));
-      vv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vs + j * rb));
-    }
+    for (int j = 0; j < kHeadGroup; ++j)
+      if (j < nh) {
+        kv[j] = *reinterpret_cast<const u32x4_t *>(kp + j * head_step);
+        vv[j] = *reinterpret_cast<const u32x4_t *>(vp + j * head_step);
+      }
 #pragma unroll
-  for (int j = 0; j < kHeadGroup; ++j)
-    if (j < nh) {
-      *reinterpret_cast<u32x4_t *>(kd + j * head_step) = kv[j];
-      *reinterpret_cast<u32x4_t *>(vd + j * head_step) = vv[j];
-    }
+    for (int j = 0; j < kHeadGroup; ++j)
+      if (j < nh) {
+        *reinterpret_cast<u32x4_t *>(kr + j * row_step) = kv[j];
+        *reinterpret_cast<u32x4_t *>(vr + j * row_step) = vv[j];
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kHeadGroup; ++j)
+      if (j < nh) {
+        kv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(kr + j * row_step));
+        vv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(vr + j * row_step));
+      }
+#pragma unroll
+    for (int j = 0; j < kHeadGroup; ++j)
+      if (j < nh) {
+        *reinterpret_cast<u32x4_t *>(kp + j * head_step) = kv[j];
+        *reinterpret_cast<u32x4_t *>(vp + j * head_step) = vv[j];
+      }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s) {
+hipError_t launch_kv_append(const AppendArgs &a, bool gather, hipStream_t s) {
   const int chunks = a.row_bytes / 16;
   int log2_chunks = 0;
   while ((1 << log2_chunks) < chunks) ++log2_chunks;
@@ -82,8 +101,9 @@ hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s) {
   const long long by = ((long long)a.Hkv + kHeadGroup - 1) / kHeadGroup;
   if (bx <= 0 || by <= 0) return hipSuccess;
   if (bx > 0x7fffffffLL || by > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)bx, (unsigned)by), dim3(256), 0, s, a,
-                     log2_chunks);
+  const dim3 grid((unsigned)bx, (unsigned)by);
+  if (gather) hipLaunchKernelGGL(kv_append_kernel<true>, grid, dim3(256), 0, s, a, log2_chunks);
+  else hipLaunchKernelGGL(kv_append_kernel<false>, grid, dim3(256), 0, s, a, log2_chunks);
   return hipGetLastError();
 }
 

@@ -244,30 +244,32 @@ RBA_EXPORT rba_status rba_prefill_fused(const void *q, const int32_t *cu_seqlens
                       d_rel, params, out, lse, stream);
 }
 
-RBA_EXPORT rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu_new,
-                                    int32_t total_new, const rba_kv_cache *kv,
-                                    const rba_page_table *pt, hipStream_t stream) {
+// Validation and launch shared by rba_kv_append and rba_kv_gather: the same
+// rows <-> pool slots mapping, copied in either direction.
+static rba_status kv_rows_copy(void *k_rows, void *v_rows, const int32_t *cu, int32_t total,
+                               const rba_kv_cache *kv, const rba_page_table *pt, bool gather,
+                               hipStream_t stream) {
   if (kv == nullptr || pt == nullptr) return RBA_ERR_INVALID_ARG;
   if (kv->dtype != RBA_BF16 && kv->dtype != RBA_F32) return RBA_ERR_INVALID_ARG;
   if (kv->num_kv_heads <= 0 || kv->head_dim <= 0) return RBA_ERR_INVALID_ARG;
   if (!is_pow2(pt->page_size)) return RBA_ERR_INVALID_ARG;
-  if (total_new < 0 || pt->num_seqs < 0 || pt->max_pages_per_seq < 0 || pt->num_pages < 0)
+  if (total < 0 || pt->num_seqs < 0 || pt->max_pages_per_seq < 0 || pt->num_pages < 0)
     return RBA_ERR_INVALID_ARG;
   if (kv->head_dim != 64 && kv->head_dim != 128) return RBA_ERR_UNSUPPORTED;
   if (pt->page_size < 16 || pt->page_size > 1024) return RBA_ERR_UNSUPPORTED;
-  if (total_new == 0 || pt->num_seqs == 0) return RBA_OK;
-  if (k_new == nullptr || v_new == nullptr || cu_new == nullptr || pt->seq_lens == nullptr ||
-      !aligned16(k_new) || !aligned16(v_new) || !pool_ok(kv, pt))
+  if (total == 0 || pt->num_seqs == 0) return RBA_OK;
+  if (k_rows == nullptr || v_rows == nullptr || cu == nullptr || pt->seq_lens == nullptr ||
+      !aligned16(k_rows) || !aligned16(v_rows) || !pool_ok(kv, pt))
     return RBA_ERR_INVALID_ARG;
   rba::AppendArgs a{};
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.cu_new = cu_new;
+  a.k_rows = k_rows;
+  a.v_rows = v_rows;
+  a.cu_new = cu;
   a.seq_lens = pt->seq_lens;
   a.block_table = pt->block_table;
   a.k_pool = const_cast<void *>(kv->k_pool);
   a.v_pool = const_cast<void *>(kv->v_pool);
-  a.total_new = total_new;
+  a.total_new = total;
   a.num_seqs = pt->num_seqs;
   a.Hkv = kv->num_kv_heads;
   a.max_pages = pt->max_pages_per_seq;
@@ -275,7 +277,20 @@ RBA_EXPORT rba_status rba_kv_append(const void *k_new, const void *v_new, const 
   a.log2_page = ilog2(pt->page_size);
   a.num_pages = pt->num_pages;
   a.row_bytes = kv->head_dim * (kv->dtype == RBA_BF16 ? 2 : 4);
-  return rba::launch_kv_append(a, stream) == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+  return rba::launch_kv_append(a, gather, stream) == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}
+
+RBA_EXPORT rba_status rba_kv_append(const void *k_new, const void *v_new, const int32_t *cu_new,
+                                    int32_t total_new, const rba_kv_cache *kv,
+                                    const rba_page_table *pt, hipStream_t stream) {
+  return kv_rows_copy(const_cast<void *>(k_new), const_cast<void *>(v_new), cu_new, total_new, kv,
+                      pt, false, stream);
+}
+
+RBA_EXPORT rba_status rba_kv_gather(void *k_out, void *v_out, const int32_t *cu_rows,
+                                    int32_t total_rows, const rba_kv_cache *kv,
+                                    const rba_page_table *pt, hipStream_t stream) {
+  return kv_rows_copy(k_out, v_out, cu_rows, total_rows, kv, pt, true, stream);
 }
 
 RBA_EXPORT int32_t rba_window_ring_pages(int32_t window, int32_t page_size, int32_t max_new) {

@@ -62,10 +62,10 @@ struct DecodeArgs {
   float sm_scale;
 };
 
-// Arguments of the K/V append kernel.
+// Arguments of the K/V append kernel (and of its reverse, the gather).
 struct AppendArgs {
-  const void *k_new;          // [total_new][Hkv][D]
-  const void *v_new;
+  void *k_rows;               // [total_new][Hkv][D]: read by the append,
+  void *v_rows;               // written by the gather
   const int32_t *cu_new;      // [B+1] over the new tokens
   const int32_t *seq_lens;    // [B] keys held after the append
   const int32_t *block_table; // [B][max_pages]
@@ -77,7 +77,7 @@ struct AppendArgs {
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_prefill_fused(const PrefillArgs &a, int head_dim, hipStream_t s);
-hipError_t launch_kv_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_kv_append(const AppendArgs &a, bool gather, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_merge(const DecodeArgs &a, int head_dim, bool bf16_out, hipStream_t s);
 hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t s);

@@ -155,3 +155,19 @@ def sample_positions(L: int, count: int, gen: torch.Generator, window: int = 0,
     while len(idx) < min(count, L):
         idx.add(int(torch.randint(0, L, (1,), generator=gen)))
     return sorted(idx)
+
+
+def random_pools(dev, dtype, Hkv, D, P, lens_after, spare_pages=3, seed=0):
+    """Random pools (no NaN) and a shuffled table with room for lens_after."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    pages_per = [max(1, -(-n // P)) for n in lens_after]
+    num_pages = sum(pages_per) + spare_pages
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.zeros((len(lens_after), max(pages_per)), dtype=torch.int32)
+    off = 0
+    for b, npg in enumerate(pages_per):
+        table[b, :npg] = perm[off:off + npg].to(torch.int32)
+        off += npg
+    k_pool = torch.randn((num_pages, Hkv, P, D), generator=g).to(dtype).to(dev)
+    v_pool = torch.randn((num_pages, Hkv, P, D), generator=g).to(dtype).to(dev)
+    return k_pool, v_pool, table.to(dev)

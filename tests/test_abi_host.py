@@ -209,8 +209,13 @@ def test_decode_split_plan():
     assert plan(1000, 0, hq=31) == (0, 0)
 
 
-def _append(kv, pt, k=FAKE, v=FAKE, cu=FAKE, total=10):
-    return rba.load().rba_kv_append(k, v, cu, total, ctypes.byref(kv), ctypes.byref(pt), None)
+# rba_kv_gather shares rba_kv_append's argument checks (the same mapping,
+# copied the other way)
+COPIES = ["rba_kv_append", "rba_kv_gather"]
+
+
+def _append(kv, pt, k=FAKE, v=FAKE, cu=FAKE, total=10, fn="rba_kv_append"):
+    return getattr(rba.load(), fn)(k, v, cu, total, ctypes.byref(kv), ctypes.byref(pt), None)
 
 
 @pytest.mark.parametrize("kwargs,expected", [
@@ -220,27 +225,30 @@ def _append(kv, pt, k=FAKE, v=FAKE, cu=FAKE, total=10):
     (dict(k=FAKE + 4), rba.RBA_ERR_INVALID_ARG),
     (dict(total=-1), rba.RBA_ERR_INVALID_ARG),
 ])
-def test_append_argument_errors(kwargs, expected):
+@pytest.mark.parametrize("fn", COPIES)
+def test_append_argument_errors(kwargs, expected, fn):
     kv, pt, _ = _layer()
-    assert _append(kv, pt, **kwargs) == expected
+    assert _append(kv, pt, fn=fn, **kwargs) == expected
 
 
-def test_append_layer_errors():
+@pytest.mark.parametrize("fn", COPIES)
+def test_append_layer_errors(fn):
     kv, pt, _ = _layer(lens=None)
-    assert _append(kv, pt) == rba.RBA_ERR_INVALID_ARG          # seq_lens is required
+    assert _append(kv, pt, fn=fn) == rba.RBA_ERR_INVALID_ARG   # seq_lens is required
     kv, pt, _ = _layer(page=48)
-    assert _append(kv, pt) == rba.RBA_ERR_INVALID_ARG          # page size not a power of two
+    assert _append(kv, pt, fn=fn) == rba.RBA_ERR_INVALID_ARG   # page size not a power of two
     kv, pt, _ = _layer(d=96)
-    assert _append(kv, pt) == rba.RBA_ERR_UNSUPPORTED
+    assert _append(kv, pt, fn=fn) == rba.RBA_ERR_UNSUPPORTED
     kv, pt, _ = _layer(page=2048)
-    assert _append(kv, pt) == rba.RBA_ERR_UNSUPPORTED
+    assert _append(kv, pt, fn=fn) == rba.RBA_ERR_UNSUPPORTED
 
 
-def test_append_empty_is_noop():
+@pytest.mark.parametrize("fn", COPIES)
+def test_append_empty_is_noop(fn):
     kv, pt, _ = _layer()
-    assert _append(kv, pt, k=None, v=None, cu=None, total=0) == rba.RBA_OK
+    assert _append(kv, pt, k=None, v=None, cu=None, total=0, fn=fn) == rba.RBA_OK
     kv, pt, _ = _layer(seqs=0)
-    assert _append(kv, pt, k=None, total=5) == rba.RBA_OK
+    assert _append(kv, pt, k=None, total=5, fn=fn) == rba.RBA_OK
 
 
 def test_window_ring_pages():

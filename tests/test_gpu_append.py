@@ -14,26 +14,10 @@ import torch
 
 import oracle
 import rba_inputs as ri
-from gpu_helpers import assert_parity, device, gpu_decode
+from gpu_helpers import assert_parity, device, gpu_decode, random_pools
 import relative_position_bias_paged_amd as rba
 
 pytestmark = pytest.mark.gpu
-
-
-def _pool_case(dev, dtype, Hkv, D, P, lens_after, spare_pages=3, seed=0):
-    """Random pools (no NaN) and a shuffled table with room for lens_after."""
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    pages_per = [max(1, -(-n // P)) for n in lens_after]
-    num_pages = sum(pages_per) + spare_pages
-    perm = torch.randperm(num_pages, generator=g)
-    table = torch.zeros((len(lens_after), max(pages_per)), dtype=torch.int32)
-    off = 0
-    for b, npg in enumerate(pages_per):
-        table[b, :npg] = perm[off:off + npg].to(torch.int32)
-        off += npg
-    k_pool = torch.randn((num_pages, Hkv, P, D), generator=g).to(dtype).to(dev)
-    v_pool = torch.randn((num_pages, Hkv, P, D), generator=g).to(dtype).to(dev)
-    return k_pool, v_pool, table.to(dev)
 
 
 def _reference_append(k_pool, v_pool, table, k_new, v_new, lens_before, new):
@@ -65,7 +49,7 @@ def test_append_writes_exactly_the_new_rows(dtype, D, P, Hkv):
     before = [0, 17, 64, 100, 31, 5]
     new = [5, 0, 1, 70, 33, 2]
     after = [a + b for a, b in zip(before, new)]
-    k_pool, v_pool, table = _pool_case(dev, dtype, Hkv, D, P, after, seed=int(D + P))
+    k_pool, v_pool, table = random_pools(dev, dtype, Hkv, D, P, after, seed=int(D + P))
     g = torch.Generator(device="cpu").manual_seed(7)
     k_new = torch.randn((sum(new), Hkv, D), generator=g).to(dtype).to(dev)
     v_new = torch.randn((sum(new), Hkv, D), generator=g).to(dtype).to(dev)
@@ -83,7 +67,7 @@ def test_append_skips_rows_outside_the_table_or_pool():
     dtype, Hkv, D, P = torch.bfloat16, 2, 128, 16
     before, new = [10, 20, 0], [4, 3, 2]
     after = [a + b for a, b in zip(before, new)]
-    k_pool, v_pool, table = _pool_case(dev, dtype, Hkv, D, P, after, seed=3)
+    k_pool, v_pool, table = random_pools(dev, dtype, Hkv, D, P, after, seed=3)
     # sequence 1: its page for the new rows is outside the pool
     table[1, 20 // P] = k_pool.shape[0] + 5
     g = torch.Generator(device="cpu").manual_seed(9)
@@ -147,7 +131,7 @@ def test_graph_captured_decode_step(W, R):
     B = len(lens0)
     cap = [n + steps for n in lens0]
     max_len = max(cap)
-    k_pool, v_pool, table = _pool_case(dev, dtype, Hkv, D, P, cap, seed=61)
+    k_pool, v_pool, table = random_pools(dev, dtype, Hkv, D, P, cap, seed=61)
     # logical keys: the initial ones are whatever the pool holds at 0 .. n0-1
     tab, kc, vc = table.cpu(), k_pool.cpu(), v_pool.cpu()
     k_log = [[kc[int(tab[b, s // P]), :, s % P, :] for s in range(n)] for b, n in enumerate(lens0)]
@@ -231,7 +215,7 @@ def test_graph_captured_mtp_verify_step():
     B = len(lens0)
     cap = [n + L * steps for n in lens0]
     max_len = max(cap)
-    k_pool, v_pool, table = _pool_case(dev, dtype, Hkv, D, P, cap, seed=81)
+    k_pool, v_pool, table = random_pools(dev, dtype, Hkv, D, P, cap, seed=81)
     tab, kc, vc = table.cpu(), k_pool.cpu(), v_pool.cpu()
     k_log = [[kc[int(tab[b, s // P]), :, s % P, :] for s in range(n)] for b, n in enumerate(lens0)]
     v_log = [[vc[int(tab[b, s // P]), :, s % P, :] for s in range(n)] for b, n in enumerate(lens0)]
