@@ -164,6 +164,40 @@ def test_decode_is_last_prefill_row():
     assert max_abs <= 2e-2
 
 
+@pytest.mark.parametrize("W,R", [(0, 1024), (300, 300)])
+def test_decode_gqa_equals_repeated_mha(W, R):
+    """GQA (4 query heads per KV head) against MHA over a pool whose K/V
+    heads are repeated per query head: the same rows within the bf16 bar,
+    and both meet the oracle."""
+    dev = device()
+    sp = spec(16, 4, 128, W, R, 64)
+    case = ri.make_decode(sp, [1, 64, 65, 1000, 5000], seed=95, device=dev)
+    G = sp.num_q_heads // sp.num_kv_heads
+    k_mha = case.k_pool.repeat_interleave(G, dim=1).contiguous()
+    v_mha = case.v_pool.repeat_interleave(G, dim=1).contiguous()
+    o_gqa = gpu_decode(case)
+    o_mha = gpu_decode(case, k_pool=k_mha, v_pool=v_mha)
+    torch.cuda.synchronize()
+    max_abs, mean_rel = errors(o_mha, o_gqa.double().cpu().numpy())
+    assert max_abs <= 2e-2 and mean_rel <= 5e-3
+    assert_parity(o_mha, oracle_decode(case), sp.dtype, "MHA twin")
+
+
+def test_decode_global_equals_window_wider_than_sequence():
+    """A global layer and a windowed layer whose window exceeds every
+    context see the same keys: equal within the bf16 bar."""
+    dev = device()
+    lens = [1, 129, 3000, 7000]
+    glob = ri.make_decode(spec(8, 2, 128, 0, 512, 64), lens, seed=97, device=dev)
+    wide = ri.DecodeCase(**{**glob.__dict__, "spec": spec(8, 2, 128, 8192, 512, 64)})
+    o_g = gpu_decode(glob)
+    o_w = gpu_decode(wide)
+    torch.cuda.synchronize()
+    max_abs, mean_rel = errors(o_w, o_g.double().cpu().numpy())
+    assert max_abs <= 2e-2 and mean_rel <= 5e-3
+    assert_parity(o_w, oracle_decode(glob), torch.bfloat16, "wide window")
+
+
 def test_nan_pages_outside_window_cannot_leak():
     """The window-only pool's page 0 is NaN and every pre-window table entry
     points at it; zeroing it must not change a single output bit."""

@@ -131,6 +131,51 @@ def test_masked_positions_cannot_leak():
     assert torch.equal(o_nan.view(torch.int16), o_bias.view(torch.int16))
 
 
+@pytest.mark.parametrize("W,R", [(0, 256), (200, 200)])
+def test_gqa_equals_repeated_mha(W, R):
+    """GQA with 4 query heads per KV head against MHA over a pool whose K/V
+    heads are repeated per query head (h -> h // G).  On a global layer every
+    head grouping visits the key tiles in the same order with the same score
+    path per tile, so the rows are bit-identical.  A windowed layer's tile
+    order rotates with the work-group's query range, which the grouping
+    changes, so there the two meet within the bf16 bar.  Both meet the
+    oracle."""
+    dev = device()
+    sp = spec(8, 2, 128, W, R, 64)
+    case = ri.make_prefill(sp, [300, 777], seed=91, device=dev, num_pages=24)
+    G = sp.num_q_heads // sp.num_kv_heads
+    k_mha = case.k_pool.repeat_interleave(G, dim=1).contiguous()
+    v_mha = case.v_pool.repeat_interleave(G, dim=1).contiguous()
+    o_gqa = gpu_prefill(case)
+    o_mha = gpu_prefill(case, k_pool=k_mha, v_pool=v_mha)
+    torch.cuda.synchronize()
+    if W <= 0:
+        assert torch.equal(o_gqa.view(torch.int16), o_mha.view(torch.int16))
+    else:
+        max_abs, mean_rel = errors(o_mha, o_gqa.double().cpu().numpy())
+        assert max_abs <= 2e-2 and mean_rel <= 5e-3
+    assert_parity(o_mha, oracle_prefill(case), sp.dtype, "MHA twin")
+
+
+@pytest.mark.parametrize("R", [64, 1024])
+def test_global_equals_window_wider_than_sequence(R):
+    """A global layer and a windowed layer whose window exceeds every
+    sequence see the same keys: equal within the bf16 bar (the two run
+    different work-group shapes), and both meet the oracle."""
+    dev = device()
+    lens = [1000, 65, 700]
+    glob = ri.make_prefill(spec(8, 2, 128, 0, R, 64), lens, seed=93, device=dev)
+    wide = ri.PrefillCase(**{**glob.__dict__, "spec": spec(8, 2, 128, 4096, R, 64)})
+    o_g = gpu_prefill(glob)
+    o_w = gpu_prefill(wide)
+    torch.cuda.synchronize()
+    max_abs, mean_rel = errors(o_w, o_g.double().cpu().numpy())
+    assert max_abs <= 2e-2 and mean_rel <= 5e-3
+    ref = oracle_prefill(glob)
+    assert_parity(o_g, ref, torch.bfloat16, "global")
+    assert_parity(o_w, ref, torch.bfloat16, "wide window")
+
+
 def test_window_one_returns_value_exactly():
     """window 1: each query sees only itself, so out[t,h] = v[t, h // G] bitwise."""
     dev = device()
