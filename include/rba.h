@@ -156,8 +156,9 @@ rba_status rba_prefill(const void *q, const int32_t *cu_seqlens,
  * rel_logits_proj [d_rel, rel_extent]); everything else as rba_prefill.
  * The products are accumulated in fp32 from the bf16 inputs and rounded
  * to bf16 before they join the score (the page's fp32 tensor, emitted in
- * bf16 as its review suggests); the clamped bucket d = R-1 of distances at
- * or beyond R-1 stays in fp32.
+ * bf16 as its review suggests), the clamped bucket d = R-1 of distances at
+ * or beyond R-1 included: the result is that of rba_prefill given the bf16
+ * bias tensor the product would materialise.
  *
  *  rel_r    bf16 [total_tokens][Hq][d_rel], 16-byte aligned
  *  w_rel_t  bf16 [rel_extent][d_rel]: W transposed (distance-major),

@@ -156,7 +156,8 @@ class Oracle:
     def prefill_projected(self, q, k, v, rel_r, w_rel, cu_q, cu_kv=None, *, window: int,
                           sm_scale: float, rows=None, want_lse: bool = False,
                           num_threads: int = 0):
-        """Prefill whose bias is the projection bias[t,h,d] = sum_k rel_r[t,h,k] w_rel[k,d].
+        """Prefill whose bias is the projection bias[t,h,d] = sum_k rel_r[t,h,k] w_rel[k,d],
+        formed in fp64 and rounded once (ties to even) to the inputs' dtype.
 
         rel_r [sum L_b, Hq, d_rel], w_rel [d_rel, R] (the pages' layout); the
         rest as ``prefill`` (cu_kv None) or ``prefill_history`` (cu_kv given).

@@ -270,18 +270,38 @@ int rba_oracle_prefill_history(int dtype, const void *q, const void *k,
 }
 
 /*
+ * Round a double to the nearest value of the given storage type, ties to
+ * even: fp32 by the C conversion (round-to-nearest-even), bf16 (8 significant
+ * bits, 8 exponent bits like fp32) directly from the double, so there is no
+ * double rounding through fp32.
+ */
+static double round_to_dtype(double x, int dtype) {
+  if (dtype == ORC_F32) return (double)(float)x;
+  if (dtype != ORC_BF16 || x == 0.0 || !isfinite(x)) return x;
+  int e;
+  frexp(x, &e);                        /* x = m * 2^e, 0.5 <= |m| < 1 */
+  if (e < -125) e = -125;              /* bf16 subnormals: fixed spacing 2^-133 */
+  const double ulp = ldexp(1.0, e - 8);
+  const double r = nearbyint(x / ulp) * ulp;   /* default mode: ties to even */
+  return fabs(r) > 0x1.fep127 ? copysign(INFINITY, r) : r;
+}
+
+/*
  * Prefill with the bias given by its projection instead of a tensor:
  *
- *   bias[t,h,d] = sum_k r[t,h,k] * w[k,d],   d = 0 .. R-1,
+ *   bias[t,h,d] = round(sum_k r[t,h,k] * w[k,d]),   d = 0 .. R-1,
  *
  * r [sum L_b, Hq, d_rel] one row per query token, w [d_rel, R]: the product
  * the TensorRT-LLM PR #17062 page's review comment on _build_rel_logits forms
  * (r of shape [T, heads, d_rel] times rel_logits_proj [d_rel, rel_extent],
- * giving the [T, heads, rel_extent] bias).  Each needed bias row is formed
- * here in fp64 from the stored r and w, then the row is attended exactly as
- * rba_oracle_prefill_history does with its bias tensor.  cu_kv NULL: no
- * history, every sequence's keys are its query tokens (rba_oracle_prefill).
- * rows, out, lse and the return value as there.
+ * giving the [T, heads, rel_extent] bias, which that comment suggests
+ * emitting in bf16).  The bias is the tensor that product materialises in the
+ * layer's dtype (the dtype of q, as for the streamed bias): each entry is
+ * formed here in fp64 from the stored r and w and rounded once to that dtype,
+ * ties to even; then the row is attended exactly as rba_oracle_prefill_history
+ * does with its bias tensor.  cu_kv NULL: no history, every sequence's keys
+ * are its query tokens (rba_oracle_prefill).  rows, out, lse and the return
+ * value as there.
  */
 int rba_oracle_prefill_projected(int dtype, const void *q, const void *k,
                                  const void *v, const void *r, const void *w,
@@ -328,7 +348,7 @@ int rba_oracle_prefill_projected(int dtype, const void *q, const void *k,
         double acc = 0.0;
         for (int kk = 0; kk < d_rel; ++kk)
           acc += elem(r, dtype, r_row + kk) * elem(w, dtype, (int64_t)kk * R + d);
-        brow[d] = acc;
+        brow[d] = round_to_dtype(acc, dtype);
       }
       attend_row(dtype, q, (tok * Hq + h) * (int64_t)D, k, v,
                  kv_first * (int64_t)Hkv * D, Hkv, D, h / G, pos, n, brow,

@@ -56,7 +56,9 @@
 // matrix cores (3 x d_rel/16 MFMAs give the 96 distances of its 32 queries),
 // rounds the products to bf16 and writes them skewed into its stage, so that
 // the same aligned stage reads as above hand each lane its four runs.  Tiles
-// at or beyond R-1 use r . W[:,R-1], formed once per row in fp32.
+// at or beyond R-1 use r . W[:,R-1], formed once per row in fp32 and rounded
+// to bf16 like the stage entries: every bias value is the product rounded
+// once to bf16, the tensor a materialised bf16 bias would hold.
 #include "rba_internal.h"
 
 #include <climits>
@@ -293,7 +295,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   //
   // Fused variant: this lane's B operand of the bias product, r[row] in
   // k-steps of 16 (lane half `half` holds elements 8*half .. 8*half+7 of
-  // each), and the clamped bucket r[row] . W[:,R-1] formed in fp32.
+  // each), and the clamped bucket r[row] . W[:,R-1] formed in fp32 and
+  // rounded to bf16.
   const uint16_t *brow = nullptr;
   float b_last;
   bool edge_wave;
@@ -310,7 +313,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
 #pragma unroll
       for (int x = 0; x < 8; ++x) part = fmaf(bf16x8_elem(rf[kk], x), bf16x8_elem(w, x), part);
     }
-    b_last = part + __shfl_xor(part, 32);
+    // rounded to bf16 like every other bias entry this variant forms
+    const float bl = part + __shfl_xor(part, 32);
+    b_last = bf16_to_f32(pack_bf16x2(bl, bl) & 0xffffu);
     edge_wave = false;
   } else {
     brow = static_cast<const uint16_t *>(a.bias) + row * R;

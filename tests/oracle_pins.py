@@ -20,6 +20,7 @@ from __future__ import annotations
 import json
 import math
 import os
+import struct
 
 import numpy as np
 import torch
@@ -49,6 +50,18 @@ def _cu(lens):
 
 def _f64(x):
     return x.detach().to(torch.float64).numpy()
+
+
+def _round_to(x, dt):
+    """x rounded to the nearest value of dtype dt, ties to even: fp32 through
+    the C float conversion (struct), bf16 (8 significant bits) directly."""
+    if dt == torch.float32:
+        return struct.unpack("f", struct.pack("f", x))[0]
+    if x == 0.0 or not math.isfinite(x):
+        return x
+    _, e = math.frexp(x)
+    e = max(e, -125)
+    return math.ldexp(round(math.ldexp(x, 8 - e)), e - 8)   # round(): ties to even
 
 
 def _brute_row(qv, keys, vals, brow, t, W, R, scale):
@@ -487,7 +500,8 @@ def _tiny_projected(seed, n_keys, n_new, Hq, Hkv, D, R, d_rel, dtype):
 
 def pin_brute_force_prefill_projected(orc):
     """Rows and LSEs against pure-Python brute force whose bias row is the
-    fsum over k of r[t,h,k] w[k,d], with and without a cached history."""
+    fsum over k of r[t,h,k] w[k,d] rounded once to the inputs' dtype, with and
+    without a cached history."""
     cases = [
         # n_keys, n_new (None: no history), Hq, Hkv, D, W, R, d_rel, dtype
         ([6, 11], None, 4, 2, 3, 0, 4, 3, torch.float32),
@@ -509,7 +523,7 @@ def pin_brute_force_prefill_projected(orc):
                 t = n - L + i
                 for h in range(Hq):
                     g = h // G
-                    brow = [math.fsum(rd[tok, h, kk] * wd[kk, d] for kk in range(d_rel))
+                    brow = [_round_to(math.fsum(rd[tok, h, kk] * wd[kk, d] for kk in range(d_rel)), dt)
                             for d in range(R)]
                     keys = [list(kd[k0 + s, g]) for s in range(n)]
                     vals = [list(vd[k0 + s, g]) for s in range(n)]
@@ -519,6 +533,33 @@ def pin_brute_force_prefill_projected(orc):
                     assert abs(lse[tok, h] - ref_lse) < 1e-12, f"lse case {ci}"
                 tok += 1
             k0 += n
+
+
+def pin_projection_rounds_like_torch(orc):
+    """r = (1, 1): the bias entry is w[0,d] + w[1,d] rounded to the dtype.
+    That sum is exact in fp32 (bf16 inputs) and in fp64 (fp32 inputs), so
+    torch's own conversion of it (round to nearest, ties to even) gives the
+    entry, and the result equals the prefill given that tensor exactly.  The
+    first columns hold exact bf16 ties: 1 + 2^-8 must round down to 1 and
+    1 + 3*2^-8 up to 1 + 2^-6."""
+    n, Hq, D, R = 10, 2, 4, 40
+    g = _gen(47)
+    for dt, wide in ((torch.bfloat16, torch.float32), (torch.float32, torch.float64)):
+        q, k, v = (_rand((n, Hq, D), g, dt), _rand((n, 1, D), g, dt), _rand((n, 1, D), g, dt))
+        r = torch.ones((n, Hq, 2), dtype=dt)
+        w = _rand((2, R), g, dt, 3.0)
+        w[0, 0], w[1, 0] = 1.0, 2.0 ** -8
+        w[0, 1], w[1, 1] = 1.0 + 2.0 ** -7, 2.0 ** -8
+        w[0, 2], w[1, 2] = -1.0, -(2.0 ** -8)
+        s = w[0].to(wide) + w[1].to(wide)
+        assert torch.equal(s.double(), w[0].double() + w[1].double())   # the sum is exact
+        b = s.to(dt)
+        if dt == torch.bfloat16:
+            assert b[0].item() == 1.0 and b[1].item() == 1.0 + 2.0 ** -6 and b[2].item() == -1.0
+        bias = b.expand(n, Hq, R).contiguous()
+        got = orc.prefill_projected(q, k, v, r, w, [0, n], window=0, sm_scale=0.5)
+        ref = orc.prefill(q, k, v, bias, [0, n], window=0, rel_extent=R, sm_scale=0.5)
+        assert np.array_equal(got, ref), str(dt)
 
 
 def pin_projection_by_permutation(orc):
@@ -603,6 +644,7 @@ ALL_PINS = [
     pin_history_single_query_is_decode,
     pin_history_rejects_more_queries_than_keys,
     pin_brute_force_prefill_projected,
+    pin_projection_rounds_like_torch,
     pin_projection_by_permutation,
     pin_projection_equal_columns_is_unbiased,
     pin_projection_last_column_is_clamped_bucket,

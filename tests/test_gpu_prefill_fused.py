@@ -72,8 +72,8 @@ def test_prefill_fused_parity(cid, sp, keys, new, d_rel):
 
 def test_fused_matches_streamed_bias():
     """The fused kernel and the streaming one given the product rounded to bf16
-    (formed here in fp32 from the same bf16 r and W) agree closely: only the
-    rounding of a few products and of the fp32 clamped bucket differ."""
+    (formed here in fp32 from the same bf16 r and W) agree closely: both add
+    the same bf16 bias, up to a rare product whose fp32 sums round apart."""
     dev = device()
     sp = spec(8, 2, 128, 0, 1024, 64)
     case = ri.make_projected(sp, [1500, 777], None, 32, seed=61, device=dev)

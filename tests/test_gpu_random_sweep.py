@@ -104,7 +104,12 @@ def test_random_fp32(i, seed):
     assert_parity(dout, oracle_decode(dec), torch.float32, f"fp32 decode #{i} {sp}")
 
 
-@pytest.mark.parametrize("i,seed", _cases("fused", 12))
+# two shapes a wider sweep of this test body found just over the bar while
+# the oracle used the unrounded product (the kernel adds a bf16 bias)
+FUSED_REGRESSION = [(476, 313197905), (960, 4105209)]
+
+
+@pytest.mark.parametrize("i,seed", _cases("fused", 12) + FUSED_REGRESSION)
 def test_random_prefill_fused(i, seed):
     rng = random.Random(seed)
     sp = _random_spec(rng)

@@ -69,6 +69,15 @@ MUTANTS = [
     ("projected rows ignore the history",
      "const int64_t pos = n - L + (tok - cu_q[b]);\n      const int64_t r_row",
      "const int64_t pos = tok - cu_q[b];\n      const int64_t r_row"),
+    ("projected bias not rounded to the dtype",
+     "brow[d] = round_to_dtype(acc, dtype);",
+     "brow[d] = acc;"),
+    ("projected bias rounded with ties away from zero",
+     "const double r = nearbyint(x / ulp) * ulp;",
+     "const double r = round(x / ulp) * ulp;"),
+    ("projected bias rounded to one bit too many",
+     "const double ulp = ldexp(1.0, e - 8);",
+     "const double ulp = ldexp(1.0, e - 9);"),
     ("no max subtraction lost in normalisation",
      "for (int i = 0; i < D; ++i) out[i] /= l;",
      "for (int i = 0; i < D; ++i) out[i] /= (l + 1e-3);"),
