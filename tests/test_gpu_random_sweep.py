@@ -4,7 +4,9 @@ and longer than the bias extent (and full causal), extents from 1 to beyond
 the sequence, page sizes 16..256, ragged and empty sequences, histories, and
 forced decode partition counts, and the prefill with the bias formed in the
 kernel (d_rel 16 or 32).  Sizes stay small enough for the oracle to check
-every row.
+every row, except in the long-sequence tests (up to 4097 prefill tokens and
+65536 decode keys, windows and extents one key off tile multiples), which
+check all heads of sampled rows when the whole output is too large.
 """
 import random
 import zlib
@@ -16,7 +18,7 @@ import torch
 import rba_inputs as ri
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, gpu_decode, gpu_prefill,
                          gpu_prefill_fused, oracle_decode, oracle_prefill, oracle_prefill_history,
-                         oracle_prefill_projected)
+                         oracle_prefill_projected, sample_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +167,52 @@ def test_random_decode_multi(i, seed):
     what = f"decode_multi #{i} {sp} q_len={q_len} lens={lens} splits={splits}"
     assert_parity(out, np.concatenate(refs), sp.dtype, what)
     assert np.max(np.abs(lse.cpu().double().numpy() - np.concatenate(ref_lses))) <= LSE_MAX_ABS, what
+
+
+# Longer sequences and windows / extents one key off a tile multiple.
+EDGE_W = [0, 0, 63, 64, 65, 127, 129, 511, 512, 513, 1000]
+EDGE_R = [1, 63, 64, 65, 511, 513, 1023, 1024, 1025, 2000]
+
+
+def _edge_spec(rng):
+    hkv = rng.choice([1, 2, 4, 8])
+    return ri.LayerSpec(num_q_heads=hkv * rng.choice([1, 2, 4, 8]), num_kv_heads=hkv,
+                        head_dim=rng.choice([64, 128, 128]), window=rng.choice(EDGE_W),
+                        rel_extent=rng.choice(EDGE_R), page_size=rng.choice([16, 64, 64, 128, 256]))
+
+
+@pytest.mark.parametrize("i,seed", _cases("long-prefill", 8))
+def test_random_long_prefill(i, seed):
+    """Sequences up to 4097 tokens: all heads of sampled query rows (every
+    tile and border case among them) when the whole output is too large."""
+    rng = random.Random(seed)
+    sp = _edge_spec(rng)
+    lens = [rng.choice([1, 63, 65, 1000, 2047, 2049, 3000, 4097]) for _ in range(rng.randint(1, 3))]
+    case = ri.make_prefill(sp, lens, seed=seed % 100000, device=device())
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    what = f"long prefill #{i} {sp} lens={lens}"
+    T = case.total_tokens
+    if T * sp.num_q_heads * max(lens) <= 3e7:
+        assert_parity(out, oracle_prefill(case), sp.dtype, what)
+        return
+    toks = sample_positions(T, 96, torch.Generator().manual_seed(seed))
+    rows = [(t, h) for t in toks for h in range(sp.num_q_heads)]
+    ref = oracle_prefill(case, rows=rows)
+    sel = torch.stack([out[t, h] for t, h in rows])
+    assert_parity(sel, ref.reshape(len(rows), -1), sp.dtype, what)
+
+
+@pytest.mark.parametrize("i,seed", _cases("long-decode", 8))
+def test_random_long_decode(i, seed):
+    """Contexts up to 65536 keys, window-only pools, partition counts up to 64."""
+    rng = random.Random(seed)
+    sp = _edge_spec(rng)
+    lens = [rng.choice([1, 64, 65, 4095, 4097, 20000, 65536]) for _ in range(rng.randint(1, 8))]
+    splits = rng.choice([0, 0, 1, 3, 16, 64])
+    wonly = sp.window > 0 and rng.random() < 0.5
+    case = ri.make_decode(sp, lens, seed=seed % 100000, device=device(), window_only=wonly)
+    out = gpu_decode(case, num_splits=splits)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_decode(case), sp.dtype,
+                  f"long decode #{i} {sp} lens={lens} splits={splits} window-only={wonly}")
