@@ -53,8 +53,8 @@ typedef enum rba_status {
   RBA_OK = 0,
   RBA_ERR_INVALID_ARG = 1, /* a null pointer, an inconsistent size, Hq % Hkv != 0,
                               page_size not a power of two, rel_extent < 1, ... */
-  RBA_ERR_UNSUPPORTED = 2, /* valid, but not a shape/dtype this build runs
-                              (see each call) */
+  RBA_ERR_UNSUPPORTED = 2, /* valid, but not a shape/dtype the library's kernels
+                              run (see each call) */
   RBA_ERR_WORKSPACE = 3,   /* workspace null or smaller than required */
   RBA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } rba_status;
