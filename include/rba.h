@@ -370,6 +370,33 @@ rba_status rba_kv_gather(void *k_out, void *v_out, const int32_t *cu_rows, int32
                          const rba_kv_cache *kv, const rba_page_table *pt, hipStream_t stream);
 
 /*
+ * Debug check of a page table against the calls that will read it: counts,
+ * on the device, the table entries a call could reach that do not name a
+ * pool page.  For sequence b holding n_b = seq_lens[b] keys, a call with up
+ * to max_new new tokens per sequence reads key positions lo_b .. n_b - 1,
+ * with lo_b = 0 on a full-causal layer (window <= 0) and
+ * max(0, n_b - max_new - window + 1) on a windowed one (rba_decode: max_new
+ * 1), i.e. entries lo_b / page_size .. (n_b - 1) / page_size.  An entry is
+ * bad if its index is at or past max_pages_per_seq or its page id is outside
+ * [0, num_pages) (the positional table of the TensorRT-LLM PR #17860 page).
+ * The attention and append kernels do not check the pages they read (a bad
+ * reachable entry is a broken caller contract); this call is how a caller
+ * checks a table in a debug run, without trapping the device.
+ *
+ *  pt           seq_lens and block_table required (device); a negative n_b
+ *               counts as no keys
+ *  max_new      >= 1
+ *  bad_entries  device int32[1], written with the count; the call clears
+ *               it on the stream first (no memset), so it needs no zeroing
+ *
+ * Nothing is allocated and no device data is read on the host, so the call
+ * can be captured in a HIP graph.  RBA_ERR_INVALID_ARG for a null pointer, a
+ * negative count, max_new < 1 or a page_size that is not a power of two.
+ */
+rba_status rba_check_page_table(const rba_page_table *pt, int32_t window, int32_t max_new,
+                                int32_t *bad_entries, hipStream_t stream);
+
+/*
  * Pages per sequence of a window-only pool for a layer with the given
  * window: a call that appends or queries at most max_new positions of a
  * sequence reads keys from at most window + max_new - 1 consecutive

@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["prefill", "prefill_fused", "decode", "decode_noalloc", "decode_num_splits",
            "decode_workspace_size", "decode_multi", "decode_multi_num_splits",
-           "decode_multi_workspace_size", "kv_append", "kv_gather", "window_ring_pages", "ring_block_table",
+           "decode_multi_workspace_size", "kv_append", "kv_gather", "check_page_table", "window_ring_pages", "ring_block_table",
            "status_string", "RbaError", "library_path", "load", "DECODE_SCRATCH_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +37,7 @@ RBA_F32 = 1
 EXPORTED = ("rba_prefill", "rba_prefill_fused", "rba_decode", "rba_decode_noalloc",
             "rba_decode_num_splits", "rba_decode_workspace_size", "rba_decode_multi",
             "rba_decode_multi_num_splits", "rba_decode_multi_workspace_size", "rba_kv_append",
-            "rba_kv_gather", "rba_window_ring_pages", "rba_ring_block_table", "rba_status_string")
+            "rba_kv_gather", "rba_check_page_table", "rba_window_ring_pages", "rba_ring_block_table", "rba_status_string")
 
 # RBA_DECODE_SCRATCH_BYTES of include/rba.h: the workspace limit of rba_decode_noalloc
 DECODE_SCRATCH_BYTES = 64 << 20
@@ -137,6 +137,9 @@ def load():
     lib.rba_kv_append.restype = ctypes.c_int
     lib.rba_kv_gather.argtypes = lib.rba_kv_append.argtypes
     lib.rba_kv_gather.restype = ctypes.c_int
+    lib.rba_check_page_table.argtypes = [P(rba_page_table), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.rba_check_page_table.restype = ctypes.c_int
     lib.rba_window_ring_pages.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     lib.rba_window_ring_pages.restype = ctypes.c_int32
     lib.rba_status_string.argtypes = [ctypes.c_int]
@@ -322,6 +325,26 @@ def kv_gather(cu_rows: torch.Tensor, total_rows: int, k_pool: torch.Tensor, v_po
                            ctypes.byref(kv), ctypes.byref(pt), _stream(stream))
     _check(st, "rba_kv_gather")
     return k_out, v_out
+
+
+def check_page_table(block_table: torch.Tensor, seq_lens: torch.Tensor, num_pages: int,
+                     page_size: int, *, window: int = 0, max_new: int = 1, out=None,
+                     stream=None) -> torch.Tensor:
+    """rba_check_page_table: the number of table entries a call with up to
+    max_new new tokens per sequence could reach that do not name a pool page,
+    as a device int32 tensor of one element (``out`` if given)."""
+    lib = load()
+    if block_table.dim() != 2 or seq_lens is None or seq_lens.numel() != block_table.shape[0]:
+        raise ValueError("block_table must be [num_seqs, max_pages] and seq_lens [num_seqs]")
+    if out is None:
+        out = torch.empty((1,), dtype=torch.int32, device=block_table.device)
+    pt = rba_page_table(_dev(block_table, "block_table", torch.int32),
+                        _dev(seq_lens, "seq_lens", torch.int32), block_table.shape[0],
+                        block_table.shape[1], int(page_size), int(num_pages))
+    st = lib.rba_check_page_table(ctypes.byref(pt), int(window), int(max_new),
+                                  _dev(out, "out", torch.int32), _stream(stream))
+    _check(st, "rba_check_page_table")
+    return out
 
 
 def window_ring_pages(window: int, page_size: int, max_new: int = 1) -> int:

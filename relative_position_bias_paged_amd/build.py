@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librba.so")
 
 SOURCES = ["prefill_bf16.hip", "decode_bf16.hip", "decode_multi.hip", "attn_f32.hip", "kv_append.hip",
-           "rba_api.cpp"]
+           "page_check.hip", "rba_api.cpp"]
 # The bf16 attention kernels never test for NaN (masking selects, it does not
 # multiply), so fmax needs no NaN-quieting of its operands.  The prefill
 # kernels are scheduled with LLVM's iterative ILP strategy: it interleaves

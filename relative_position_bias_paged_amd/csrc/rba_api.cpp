@@ -293,6 +293,29 @@ RBA_EXPORT rba_status rba_kv_gather(void *k_out, void *v_out, const int32_t *cu_
   return kv_rows_copy(k_out, v_out, cu_rows, total_rows, kv, pt, true, stream);
 }
 
+RBA_EXPORT rba_status rba_check_page_table(const rba_page_table *pt, int32_t window,
+                                           int32_t max_new, int32_t *bad_entries,
+                                           hipStream_t stream) {
+  if (pt == nullptr || bad_entries == nullptr || max_new < 1) return RBA_ERR_INVALID_ARG;
+  if (!is_pow2(pt->page_size) || pt->num_seqs < 0 || pt->max_pages_per_seq < 0 ||
+      pt->num_pages < 0)
+    return RBA_ERR_INVALID_ARG;
+  if (pt->num_seqs > 0 && (pt->seq_lens == nullptr ||
+                           (pt->max_pages_per_seq > 0 && pt->block_table == nullptr)))
+    return RBA_ERR_INVALID_ARG;
+  rba::PageCheckArgs a{};
+  a.block_table = pt->block_table;
+  a.seq_lens = pt->seq_lens;
+  a.bad = bad_entries;
+  a.num_seqs = pt->num_seqs;
+  a.max_pages = pt->max_pages_per_seq;
+  a.log2_page = ilog2(pt->page_size);
+  a.num_pages = pt->num_pages;
+  a.window = window > 0 ? window : 0;
+  a.max_new = max_new;
+  return rba::launch_page_check(a, stream) == hipSuccess ? RBA_OK : RBA_ERR_HIP;
+}
+
 RBA_EXPORT int32_t rba_window_ring_pages(int32_t window, int32_t page_size, int32_t max_new) {
   if (window <= 0 || max_new < 1 || !is_pow2(page_size)) return 0;
   const long long span = (long long)window + max_new - 1;      // consecutive key positions read

@@ -75,6 +75,14 @@ struct AppendArgs {
   int32_t row_bytes;          // head_dim * element size, a multiple of 16
 };
 
+// Arguments of the page-table check.
+struct PageCheckArgs {
+  const int32_t *block_table; // [B][max_pages]
+  const int32_t *seq_lens;    // [B] keys held
+  int32_t *bad;               // [1] count written
+  int32_t num_seqs, max_pages, log2_page, num_pages, window, max_new;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_prefill_fused(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_kv_append(const AppendArgs &a, bool gather, hipStream_t s);
@@ -84,5 +92,6 @@ hipError_t launch_decode_plan(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_decode_multi(const DecodeArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_page_check(const PageCheckArgs &a, hipStream_t s);
 
 }  // namespace rba

@@ -251,6 +251,23 @@ def test_append_empty_is_noop(fn):
     assert _append(kv, pt, k=None, total=5, fn=fn) == rba.RBA_OK
 
 
+def test_check_page_table_argument_errors():
+    lib = rba.load()
+    _, pt, _ = _layer()
+
+    def call(p=pt, window=0, max_new=1, out=FAKE):
+        return lib.rba_check_page_table(ctypes.byref(p) if p is not None else None, window, max_new,
+                                        out, None)
+
+    assert call(p=None) == rba.RBA_ERR_INVALID_ARG
+    assert call(out=None) == rba.RBA_ERR_INVALID_ARG
+    assert call(max_new=0) == rba.RBA_ERR_INVALID_ARG
+    _, bad_page, _ = _layer(page=48)
+    assert call(p=bad_page) == rba.RBA_ERR_INVALID_ARG
+    _, no_lens, _ = _layer(lens=None)
+    assert call(p=no_lens) == rba.RBA_ERR_INVALID_ARG
+
+
 def test_window_ring_pages():
     # window 512, 64-token pages, one new token: 512 positions span 9 pages
     assert rba.window_ring_pages(512, 64, 1) == 9

@@ -1,4 +1,5 @@
-"""GPU tests of rba_kv_gather, the reverse of rba_kv_append.
+"""GPU tests of rba_kv_gather, the reverse of rba_kv_append, and of the
+page-table check rba_check_page_table.
 
 De-paging whole sequences through shuffled page tables returns, byte for
 byte, the logical K/V the pools were filled from. This covers page sizes
@@ -6,8 +7,11 @@ below, at and above the 64-key tile, and lengths on both sides of page
 borders (the positional page table of the TensorRT-LLM PR #17860 page). A
 window-only decode pool gives back its last W positions. A gather with the
 arguments of an append returns the appended rows. Rows whose position or page
-id is out of range are left unwritten.
+id is out of range are left unwritten. The page-table check counts exactly the
+reachable entries that name no pool page, against a plain Python count.
 """
+import random
+
 import pytest
 import torch
 
@@ -114,3 +118,58 @@ def test_gather_leaves_unreachable_rows_unwritten():
                 page = int(tab[b, i // P])
                 assert torch.equal(_bytes(k_out[r]), _bytes(k_pool[page, :, i % P])), (b, i)
                 assert torch.equal(_bytes(v_out[r]), _bytes(v_pool[page, :, i % P])), (b, i)
+
+
+def _count_bad(table, lens, num_pages, P, window, max_new):
+    """Reachable entries naming no pool page, counted in plain Python."""
+    bad = 0
+    for b, n in enumerate(lens):
+        n = max(n, 0)
+        if n == 0:
+            continue
+        lo = max(0, n - max_new - window + 1) if window > 0 else 0
+        for j in range(lo // P, (n - 1) // P + 1):
+            if j >= len(table[b]) or not 0 <= table[b][j] < num_pages:
+                bad += 1
+    return bad
+
+
+def test_check_page_table_cases():
+    dev = device()
+    P, num_pages = 16, 40
+    table = [[(7 * b + j) % num_pages for j in range(8)] for b in range(5)]
+    table[0][2] = -1                  # reachable on a global layer
+    table[1][7] = num_pages           # past sequence 1's keys: unreachable
+    table[3][0] = num_pages + 9       # before the window of a long sequence
+    lens = [40, 100, 8 * P + 20, 8 * P, -3]    # sequence 2 runs past the table
+    t = torch.tensor(table, dtype=torch.int32, device=dev)
+    n = torch.tensor(lens, dtype=torch.int32, device=dev)
+    out = torch.full((1,), 12345, dtype=torch.int32, device=dev)   # no zeroing needed
+    for window, max_new in ((0, 1), (40, 1), (40, 8), (1000, 1)):
+        got = rba.check_page_table(t, n, num_pages, P, window=window, max_new=max_new, out=out)
+        torch.cuda.synchronize()
+        ref = _count_bad(table, lens, num_pages, P, window, max_new)
+        assert int(got.item()) == ref, (window, max_new, int(got.item()), ref)
+    assert _count_bad(table, lens, num_pages, P, 0, 1) == 1 + 2 + 1   # -1, two past the table, window-free
+    empty = rba.check_page_table(t[:0], n[:0], num_pages, P)
+    torch.cuda.synchronize()
+    assert int(empty.item()) == 0
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_check_page_table_random(seed):
+    dev = device()
+    rng = random.Random(seed)
+    P = rng.choice([16, 64, 256])
+    B, max_pages, num_pages = rng.randint(1, 40), rng.randint(1, 70), rng.randint(1, 500)
+    table = [[rng.randrange(num_pages) if rng.random() > 0.05 else rng.choice([-1, num_pages, 10 ** 6])
+              for _ in range(max_pages)] for _ in range(B)]
+    lens = [rng.choice([0, 1, P, P + 1, rng.randint(1, max_pages * P), max_pages * P + 5])
+            for _ in range(B)]
+    window = rng.choice([0, 0, 1, 17, 512])
+    max_new = rng.choice([1, 1, 4, 100])
+    got = rba.check_page_table(torch.tensor(table, dtype=torch.int32, device=dev),
+                               torch.tensor(lens, dtype=torch.int32, device=dev), num_pages, P,
+                               window=window, max_new=max_new)
+    torch.cuda.synchronize()
+    assert int(got.item()) == _count_bad(table, lens, num_pages, P, window, max_new)
