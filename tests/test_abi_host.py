@@ -251,6 +251,54 @@ def test_append_empty_is_noop(fn):
     assert _append(kv, pt, k=None, total=5, fn=fn) == rba.RBA_OK
 
 
+_LAYOUT_C = r"""
+#include <stdio.h>
+#include "rba.h"
+#define F(s, f) printf("%s %s %zu\n", #s, #f, offsetof(s, f))
+int main(void) {
+  printf("rba_page_table * %zu\n", sizeof(rba_page_table));
+  F(rba_page_table, block_table); F(rba_page_table, seq_lens); F(rba_page_table, num_seqs);
+  F(rba_page_table, max_pages_per_seq); F(rba_page_table, page_size); F(rba_page_table, num_pages);
+  printf("rba_kv_cache * %zu\n", sizeof(rba_kv_cache));
+  F(rba_kv_cache, k_pool); F(rba_kv_cache, v_pool); F(rba_kv_cache, num_kv_heads);
+  F(rba_kv_cache, head_dim); F(rba_kv_cache, dtype);
+  printf("rba_attn_params * %zu\n", sizeof(rba_attn_params));
+  F(rba_attn_params, num_q_heads); F(rba_attn_params, window); F(rba_attn_params, rel_extent);
+  F(rba_attn_params, sm_scale);
+  printf("enum * %zu\n", sizeof(rba_status) + 0 * sizeof(rba_dtype));
+  return 0;
+}
+"""
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The binding's ctypes structs against the header compiled as C (gcc):
+    every size and field offset agrees, so a C caller and the binding pass
+    the same bytes."""
+    src = tmp_path / "layout.c"
+    src.write_text(_LAYOUT_C)
+    exe = tmp_path / "layout"
+    inc = os.path.join(ROOT, "include")
+    res = subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", inc,
+                          "-I", "/opt/rocm/include", str(src), "-o", str(exe)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    seen = 0
+    for line in filter(None, out):
+        name, field, value = line.split()
+        if name == "enum":
+            assert int(value) == ctypes.sizeof(ctypes.c_int)
+            continue
+        cls = getattr(rba, name)
+        if field == "*":
+            assert ctypes.sizeof(cls) == int(value), name
+        else:
+            assert getattr(cls, field).offset == int(value), (name, field)
+        seen += 1
+    assert seen == 18
+
+
 def test_check_page_table_argument_errors():
     lib = rba.load()
     _, pt, _ = _layer()
