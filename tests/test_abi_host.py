@@ -299,6 +299,16 @@ def test_struct_layouts_match_the_header(tmp_path):
     assert seen == 18
 
 
+def test_c_abi_check_program_builds(tmp_path):
+    """The plain-C check program of the GPU tests compiles and links against
+    the header, librba.so, the oracle's library and the HIP runtime."""
+    import sys
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import c_abi_build
+    out = c_abi_build.build(str(tmp_path / "c_abi_check"))
+    assert os.path.getsize(out) > 0
+
+
 def test_check_page_table_argument_errors():
     lib = rba.load()
     _, pt, _ = _layer()
