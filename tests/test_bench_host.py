@@ -64,7 +64,9 @@ def test_time_steps_warms_for_the_minimum_time():
     _, _, warm_steps, warm_ms = bench.time_steps(step, steps=2, warmup=2, torch=_fake_torch(log),
                                                  min_warm_ms=30.0)
     first = log.index("event")
-    assert log[:first].count("step") >= 15       # at least 30 ms of 2 ms steps
+    # the warm-up ran on past its 2 steps until 30 ms had passed (each step
+    # sleeps at least 2 ms, often more on a busy host, so no exact count)
+    assert log[:first].count("step") > 2
     assert warm_steps == log[:first].count("step") and warm_ms >= 30.0
     assert log[first:].count("step") == 2
 
