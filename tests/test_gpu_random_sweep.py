@@ -7,7 +7,10 @@ kernel (d_rel 16 or 32).  Sizes stay small enough for the oracle to check
 every row, except in the long-sequence tests (up to 4097 prefill tokens and
 65536 decode keys, windows and extents one key off tile multiples), which
 check all heads of sampled rows when the whole output is too large.
+RBA_SWEEP_SCALE=k runs k times as many cases of every test (a 6000-case run
+of the short tests and an 800-case run of the long ones pass).
 """
+import os
 import random
 import zlib
 
@@ -34,6 +37,9 @@ def _random_spec(rng, dtype=torch.bfloat16):
 
 
 def _cases(kind, n):
+    """n seeded cases per test (RBA_SWEEP_SCALE multiplies n for a deeper
+    sweep; the first n cases stay the same)."""
+    n *= max(1, int(os.environ.get("RBA_SWEEP_SCALE", "1")))
     rng = random.Random(zlib.crc32(kind.encode()))
     return [(i, rng.randrange(1 << 30)) for i in range(n)]
 
