@@ -597,11 +597,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       }
     };
     auto max16 = [&](const f32x16_t &acc) {
-      float m4[4];
+      // a chain of two-input maxes, which the compiler fuses into v_max3
+      float m = fmaxf(acc[0], acc[1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        m4[i] = fmaxf(fmaxf(acc[4 * i + 0], acc[4 * i + 1]), fmaxf(acc[4 * i + 2], acc[4 * i + 3]));
-      return fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      for (int j = 2; j < 16; j += 2) m = fmaxf(fmaxf(m, acc[j]), acc[j + 1]);
+      return m;
     };
     // P = exp2(score - max) in bf16, as the PV MFMA consumes it; the row sum
     // adds exactly these rounded values, two per v_dot2 against (1, 1).
