@@ -234,20 +234,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // pq0..pq0+31, each test one compare with a per-wave bound (d = p - s
   // ranges over [pq0 - s0 - 63, pq0 + 31 - s0]):
   //   active     s_lo < s0 <= s_hi  some key is visible
-  //   band       s0 > s_band        some distance is below R-1 (bias staged)
+  //   band       s0 > s_band        some distance is below R-1, or at most
+  //                                 R-1 on narrow layers (bias staged)
   //   masked     s0 > s_diag, s0 <= s_wedge or s0 > s_tail
   //              (causal diagonal, window edge, sequence end inside the tile)
   //   beyond     s0 <= s_strad      some distance exceeds R-1
   const int s_hi = pq0 + 31;
   const int s_lo = (W > 0) ? pq0 - (BN - 1) - W : INT_MIN;
-  const int s_band = pq0 - (BN - 2) - R;
+  // A layer whose window stays within the R buckets (narrow) never sees a
+  // distance beyond R-1 inside its window.  With the streamed bias, its band
+  // also takes the tiles whose smallest distance is exactly R-1: the stage
+  // then holds every visible distance, bucket R-1 included, and the clamped
+  // bucket is never read on its own.
+  const bool wide_layer = W <= 0 || W > R;
+  const int s_band = pq0 - (BN - 2) - R - ((FUSED || wide_layer) ? 0 : 1);
   const int s_diag = pq0 - (BN - 1);
   const int s_wedge = (W > 0) ? pq0 + 31 - W : INT_MIN;
   const int s_tail = n_k - BN;
   const int s_strad = pq0 + 31 - R;
-  // a layer whose window stays within the R buckets never sees a clamped
-  // distance inside its window
-  const bool wide_layer = W <= 0 || W > R;
   // The same tests as single unsigned range compares, s0 - lo - 1 < span
   // (tiles are never below 0, so lower bounds under -1 are clamped to -1):
   //   active     lo = max(s_lo, -1),        up to s_hi
@@ -291,7 +295,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // stay inside the bias tensor except for rows within 1024 elements of
   // either end of it: waves holding such a row read element by element with
   // distances clamped to [0, R) instead.  Values read outside [0, R) are
-  // masked or replaced by the clamped bucket.
+  // masked or replaced by the clamped bucket, which only wide layers use
+  // (narrow ones never read it).
   //
   // Fused variant: this lane's B operand of the bias product, r[row] in
   // k-steps of 16 (lane half `half` holds elements 8*half .. 8*half+7 of
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     edge_wave = false;
   } else {
     brow = static_cast<const uint16_t *>(a.bias) + row * R;
-    b_last = bf16_to_f32(brow[R - 1]);
+    b_last = wide_layer ? bf16_to_f32(brow[R - 1]) : 0.f;
     const long long row_off = (long long)row * R;
     const long long bias_elems = (long long)a.total_tokens * Hq * R;
     edge_wave = __ballot(row_off < 1024 || bias_elems - row_off < R + 1024) != 0;
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         const int kv_lo1 = (W > 0) ? dq - W + 1 : -(1 << 30);
         const uint32_t span = (uint32_t)max(kv_hi - kv_lo1 + 1, 0);
         if (clamp_free) {
-          // every visible distance is below R-1 or equals it (bias[R-1] = b_last)
+          // every visible distance is at most R-1: all of them are staged
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int koff = 32 * sub + 16 * (j >> 3) + (j & 7);

@@ -121,6 +121,55 @@ def test_null_seq_lens_is_plain_prefill():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+# History lengths whose remainders mod 32 put a 64-key tile's smallest
+# distance exactly at R-1 for some query block (R = 128: 30; R = 98: 0;
+# R = 100: 2), next to others.
+LAST_BUCKET_HIST = [0, 2, 30, 31, 33, 62, 97]
+LAST_BUCKET_NEW = [160, 97, 130, 64, 1, 200, 150]
+
+
+@pytest.mark.parametrize("W,R,dtype", [(128, 128, torch.bfloat16), (98, 98, torch.bfloat16),
+                                       (100, 100, torch.bfloat16), (64, 128, torch.bfloat16),
+                                       (300, 128, torch.bfloat16), (0, 128, torch.bfloat16),
+                                       (100, 100, torch.float32)])
+def test_dominant_last_bucket(W, R, dtype):
+    """Bucket R-1 set to 6 in every bias row, the rest N(0, 1): the keys at
+    distance R-1 and beyond that the window shows carry most of the softmax
+    weight, so a wrong value for that bucket, or a lost key at distance
+    exactly R-1 (a window of R keys ends there), moves those rows far past
+    the bar."""
+    dev = device()
+    sp = spec(4, 2, 128, W, R, 64, dtype=dtype)
+    keys = [h + n for h, n in zip(LAST_BUCKET_HIST, LAST_BUCKET_NEW)]
+    case = ri.make_prefill_history(sp, keys, LAST_BUCKET_NEW, seed=7 * R + W, device=dev)
+    case.bias[..., R - 1] = 6.0
+    out = gpu_prefill(case)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_prefill_history(case), dtype, f"W={W} R={R}")
+
+
+@pytest.mark.parametrize("W", [128, 100])
+def test_narrow_window_ignores_buckets_it_cannot_reach(W):
+    """A window of W <= R keys never reaches a distance above W-1: bias
+    columns W.. set to NaN change nothing, bit for bit, against the same
+    layer with only W columns (bucket W-1 large, so that its use counts)."""
+    dev = device()
+    sp = spec(4, 2, 128, W, W, 64)
+    keys = [h + n for h, n in zip(LAST_BUCKET_HIST, LAST_BUCKET_NEW)]
+    case = ri.make_prefill_history(sp, keys, LAST_BUCKET_NEW, seed=W, device=dev)
+    case.bias[..., W - 1] = 6.0
+    wide_bias = torch.full((*case.bias.shape[:2], 2 * W + 8), float("nan"), dtype=case.bias.dtype,
+                           device=dev)
+    wide_bias[..., :W] = case.bias
+    o1 = gpu_prefill(case)
+    o2 = rba.prefill(case.q, case.cu_seqlens, case.max_seqlen, case.k_pool, case.v_pool,
+                     case.block_table, case.seq_lens_dev, wide_bias, window=W,
+                     sm_scale=sp.scale())
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert_parity(o1, oracle_prefill_history(case), torch.bfloat16, f"W={W}")
+
+
 @pytest.mark.parametrize("name", ["chunked-local-4x512-ctx4096", "chunked-global-2x2048-ctx16384"])
 def test_chunked_workload_sampled(name):
     """The chunked-prefill benchmark workloads at full size, checked on every
