@@ -439,7 +439,9 @@ def line(name, args, torch, rba, ri, oracle_budget):
                 rba.prefill_fused(h.q, h.cu_seqlens, h.max_seqlen, h.k_pool, h.v_pool,
                                   h.block_table, h.seq_lens_dev, case.rel_r, case.w_rel_t,
                                   window=sp.window, sm_scale=sp.scale(), out=out)
-            kernel = f"prefill_bf16_kernel<128, 8 waves, d_rel {case.d_rel}> (bias formed in the kernel)"
+            nw = 4 if sp.window > 0 and (sp.num_q_heads // sp.num_kv_heads) % 2 == 0 else 8
+            kernel = (f"prefill_bf16_kernel<{sp.head_dim}, {nw} waves, d_rel {case.d_rel}> "
+                      "(bias formed in the kernel)")
         else:
             def step():
                 rba.prefill(h.q, h.cu_seqlens, h.max_seqlen, h.k_pool, h.v_pool, h.block_table,

@@ -133,13 +133,18 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
 // 11:8) that waits for LDS and scalar memory traffic only.
 constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
 
-// Fused stage layout: row q of a wave's stage starts at element 32 + 104*q
-// and holds distance index e (0..63 in use) at +e.  The product for distance
-// index idx = e + q of query q is written at 32 + 103*q + idx, so a lane's
-// writes sit at fixed offsets from one per-lane base; the indices it also
-// computes outside 0..63 (-31..95) land in the unused elements 64..103 of its
-// own or the previous row, or in the 32-element head.  Rows 208 bytes apart
-// put the 16 rows one aligned 16-byte read serves on distinct banks.
+// Fused stage layout: two parts of 16 query rows.  Row r of a part starts at
+// element 32 + 104*r and holds distance index e (0..63 in use) at +e.  The
+// product for distance index idx = e + q of query q = 16*hi + r is written at
+// 32 + 103*r - 16*hi + idx of part hi, so a lane's writes sit at fixed offsets
+// from one per-lane base; the indices it also computes outside 0..63
+// (-31..95) land in the unused elements 64..103 of its own or the previous
+// row, or in the part's 32-element head (every write stays in elements
+// 16..1671 of its part).  Rows 208 bytes apart put the 16 rows one aligned
+// 16-byte read serves on distinct banks.  The two parts are either one
+// stage of 32 rows (part 1 = part 0 + 16 rows) or, in 4-wave work-groups over
+// head_dim 128, the wave's own 4 KiB slices of the next K and V buffers,
+// which are free until the wave issues its loads of the next tile.
 constexpr int FUSED_ROW = 104;
 // chunk swizzle of W^T row r in the fused variant's LDS buffers: rows are
 // 2*DR bytes, 128/DR of them fill the 64 banks, so the swizzle steps once
@@ -153,26 +158,40 @@ constexpr int FUSED_STAGE = 32 + 32 * FUSED_ROW;
 template <int D, int NW, bool BIG_PAGE, bool VEC_BIAS, int DR>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr bool FUSED = DR > 0;                // bias formed from r and W^T
-  static_assert(!FUSED || (NW == 8 && (DR == 16 || DR == 32)), "fused variant: 8 waves, d_rel 16 or 32");
+  static_assert(!FUSED || ((NW == 8 || NW == 4) && (DR == 16 || DR == 32)),
+                "fused variant: 4 or 8 waves, d_rel 16 or 32");
+  // fused, 4 waves, head_dim 128: the bias stage lives in the next K/V buffer
+  // (two work-groups then fit a CU's LDS)
+  constexpr bool ALIAS = FUSED && NW == 4 && D == 128;
   constexpr int CHUNKS = D / 8;                 // 16-byte chunks per key row
   constexpr int KB = D / 16;                    // MFMA k-steps over head_dim
   constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
   constexpr int ROWS_PER_DMA = 512 / D;         // key rows per 1 KiB LDS write
   constexpr int DMA_PER_WAVE = BN * D / 512 / NW;  // 1 KiB writes per wave per matrix
+  // a fused stage part (writes up to element 32 + 15*103 + 4 + 91) fits the
+  // wave's slice of a K or V buffer
+  static_assert(!ALIAS || DMA_PER_WAVE * 512 > 32 + 15 * (FUSED_ROW - 1) + 4 + 91, "stage part too large");
   // two K/V buffers as separate objects, so the compiler can tell that the
   // direct loads into one do not alias reads of the other
   __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
   __shared__ __align__(16) uint16_t k_lds1[BN * D], v_lds1[BN * D];
   // bias stage: per wave, 32 rows x 64 distances, 16-byte chunks of row r
   // XOR-swizzled by (r/2) mod 8 so the lanes' aligned reads avoid bank
-  // conflicts (fused variant: the skewed layout above, unswizzled)
+  // conflicts (fused variant: the skewed layout above, unswizzled; none when
+  // it lives in the K/V buffers)
   constexpr int STAGE_W = FUSED ? FUSED_STAGE : 32 * BN;
-  __shared__ __align__(16) uint16_t bias_stage[NW * STAGE_W];
+  uint16_t *stage_base = nullptr;
+  if constexpr (!ALIAS) {
+    __shared__ __align__(16) uint16_t bias_stage[NW * STAGE_W];
+    stage_base = bias_stage;
+  }
   // fused variant: two buffers of W^T rows (distances P0-s0-63 .. P0+QM-1-s0
-  // of tile s0, P0 the work-group's first query position), at most 32*NW+64
-  // rows of DR elements; the 16-byte chunks of row r are XOR-swizzled by
-  // wsl_swizzle(r) so that 16 consecutive rows read on distinct banks
-  constexpr int WSL_ROWS = 32 * NW + 64;
+  // of tile s0, P0 the work-group's first query position), QM+64 rows of DR
+  // elements: at most 32*NW+64, and 128 in 4-wave work-groups, which the
+  // host gives at least two heads (QM <= 64); the 16-byte chunks of row r are
+  // XOR-swizzled by wsl_swizzle(r) so that 16 consecutive rows read on
+  // distinct banks
+  constexpr int WSL_ROWS = NW == 4 ? 128 : 32 * NW + 64;
   uint16_t *wsl0 = nullptr, *wsl1 = nullptr;
   if constexpr (FUSED) {
     __shared__ __align__(16) uint16_t w_sl0[WSL_ROWS * DR], w_sl1[WSL_ROWS * DR];
@@ -206,6 +225,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int qt = nqt - 1 - rr / ngroups;
   const int hg = rr % ngroups;
   const int QM = 32 * (NW / hpw);            // queries per head per work-group
+  if constexpr (FUSED && WSL_ROWS < 32 * NW + 64) {
+    if (QM + 64 > WSL_ROWS) return;          // W^T rows would not fit (the host never asks)
+  }
   // this wave: head slot wave % hpw, query block wave / hpw
   const int h = kvh * a.G + hg * hpw + wave % hpw;
   const int qb = wave / hpw;
@@ -392,7 +414,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // i.e. the keys s0 + 32*sub + 16*G + 8*half + 7 down to + 0: chunk
   // 7 - half - 2p of the row's 64 staged distances t - s0 - 63 .. t - s0.
   const bool use_stage = FUSED || (VEC_BIAS && !edge_wave);
-  uint16_t *stage_w = bias_stage + wave * STAGE_W;
+  uint16_t *stage_w = ALIAS ? nullptr : stage_base + wave * STAGE_W;
+  // Fused stage part of this lane's query row, given the step's next K/V
+  // buffers, and this lane's offsets in it: write base (element 4*half of
+  // distance index 0) and row start.
+  // (One stage: parts 0 and 1 are contiguous, so rows count from part 0.)
+  auto fused_part = [&](uint16_t *kn, uint16_t *vn) {
+    if constexpr (ALIAS) return (col < 16 ? kn : vn) + DMA_PER_WAVE * wave * 512;
+    else return stage_w;
+  };
+  const int frow = ALIAS ? (col & 15) : col;
+  const int fw_off = 32 + (FUSED_ROW - 1) * frow - (ALIAS ? 16 * (col >> 4) : 0) + 4 * half;
+  const int fr_off = 32 + FUSED_ROW * frow;
   // Stage write k of this lane: row 8k + lane/8 of the wave, physical chunk
   // lane%8 = logical chunk c ^ swizzle.  Pointer for tile 0; tile s0 is
   // s0 elements lower.
@@ -410,11 +443,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
 #pragma unroll
     for (int k = 0; k < 4; ++k) dma16(sptr[k] - 2 * (long long)s0, (lds_void_t *)(stage_w + k * 512));
   };
-  auto load_bias = [&](int s0, u32x4_t (&bp)[4]) {
+  auto load_bias = [&](int s0, u32x4_t (&bp)[4], const uint16_t *part) {
     if constexpr (FUSED) {
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        bp[p] = *reinterpret_cast<const u32x4_t *>(stage_w + 32 + col * FUSED_ROW + (7 - half - 2 * p) * 8);
+        bp[p] = *reinterpret_cast<const u32x4_t *>(part + fr_off + (7 - half - 2 * p) * 8);
     } else if (use_stage) {
       const int sw = (col >> 1) & 7;
 #pragma unroll
@@ -464,8 +497,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   // over 96 distance indices in three 32-row MFMA blocks (A = W^T rows from
   // the buffer, B = r), rounded to bf16.  Register 4i+j of block b holds
   // index idx = 32b + 8i + 4*half + j of query col, written at
-  // 32 + 103*col + idx of the stage.
-  auto fuse_bias = [&](const uint16_t *wsl) {
+  // fw_off - 4*half + idx of the lane's stage part.
+  auto fuse_bias = [&](const uint16_t *wsl, uint16_t *part) {
     if constexpr (FUSED) {
       // row 32*qb + 32*b + col, logical chunk 2*kk + half (the swizzle of a
       // row depends on col only: 32 rows are whole swizzle periods)
@@ -474,7 +507,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       // 2-byte stores, kept apart: merged into 8-byte ones they would sit at
       // 2-byte-aligned addresses, which LDS serves with long stalls
       typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
-      volatile lds_u16_t *sb = (volatile lds_u16_t *)(stage_w + 32 + (FUSED_ROW - 1) * col + 4 * half);
+      volatile lds_u16_t *sb = (volatile lds_u16_t *)(part + fw_off);
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         f32x16_t acc;
@@ -732,10 +765,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int s0 = s_cur;
     const bool more = --steps_left > 0;
     if (!FIXED && wave_band(s0)) {
-      fuse_bias(wc);
-      load_bias(s0, bias_r);
+      uint16_t *part = fused_part(kn, vn);
+      fuse_bias(wc, part);
+      load_bias(s0, bias_r, part);
     }
     if (more) {
+      // a stage in the next K/V buffers: this lane's reads of it must be
+      // done before the loads below overwrite it
+      if constexpr (ALIAS) __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
       load_kv(s_nxt, page_nxt, kn, vn);
       page_nxt = tile_page(s_nxt2);
       if constexpr (FUSED) {
@@ -823,11 +860,25 @@ static void launch_d(const PrefillArgs &a, hipStream_t s) {
   else hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, false, 0>), grid, block, 0, s, a);
 }
 
-template <int D, int DR>
+template <int D, int NW, int DR>
 static void launch_fused_d(const PrefillArgs &a, hipStream_t s) {
-  dim3 grid(a.num_blocks), block(64 * 8);
-  if (a.page_size >= BN) hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, true, true, DR>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((prefill_bf16_kernel<D, 8, false, true, DR>), grid, block, 0, s, a);
+  dim3 grid(a.num_blocks), block(64 * NW);
+  if (a.page_size >= BN) hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, true, true, DR>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((prefill_bf16_kernel<D, NW, false, true, DR>), grid, block, 0, s, a);
+}
+
+template <int NW>
+static hipError_t launch_fused_nw(const PrefillArgs &a, int head_dim, hipStream_t s) {
+  if (head_dim == 128) {
+    if (a.d_rel == 32) launch_fused_d<128, NW, 32>(a, s);
+    else launch_fused_d<128, NW, 16>(a, s);
+  } else if (head_dim == 64) {
+    if (a.d_rel == 32) launch_fused_d<64, NW, 32>(a, s);
+    else launch_fused_d<64, NW, 16>(a, s);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s) {
@@ -845,17 +896,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, int head_dim, hipStream_t s
 }
 
 hipError_t launch_prefill_fused(const PrefillArgs &a, int head_dim, hipStream_t s) {
-  if (a.waves != 8 || (a.d_rel != 16 && a.d_rel != 32)) return hipErrorInvalidValue;
-  if (head_dim == 128) {
-    if (a.d_rel == 32) launch_fused_d<128, 32>(a, s);
-    else launch_fused_d<128, 16>(a, s);
-  } else if (head_dim == 64) {
-    if (a.d_rel == 32) launch_fused_d<64, 32>(a, s);
-    else launch_fused_d<64, 16>(a, s);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.d_rel != 16 && a.d_rel != 32) return hipErrorInvalidValue;
+  // 4-wave work-groups hold W^T rows for at most 64 queries: two heads or more
+  if (a.waves == 4 && a.hpw >= 2) return launch_fused_nw<4>(a, head_dim, s);
+  if (a.waves == 8) return launch_fused_nw<8>(a, head_dim, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace rba

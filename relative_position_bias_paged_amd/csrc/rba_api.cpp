@@ -200,8 +200,10 @@ rba_status prefill_impl(const void *q, const int32_t *cu_seqlens, int32_t total_
   if (kv->dtype == RBA_BF16) {
     // Query heads of one KV head share a work-group (and its K/V tiles):
     // the largest of 8, 4, 2, 1 that divides both G and the wave count.
-    // The fused variant runs 8 waves on every layer.
-    a.waves = (a.window > 0 && !fused) ? RBA_PREFILL_WAVES_LOCAL : RBA_PREFILL_WAVES_GLOBAL;
+    // The fused variant takes the local wave count only where G is even (its
+    // 4-wave work-groups need two heads or more), else 8 waves.
+    a.waves = (a.window > 0 && (!fused || a.G % 2 == 0)) ? RBA_PREFILL_WAVES_LOCAL
+                                                          : RBA_PREFILL_WAVES_GLOBAL;
     a.hpw = 1;
     while (a.hpw * 2 <= a.waves && a.G % (a.hpw * 2) == 0) a.hpw *= 2;
     const int qm = 32 * (a.waves / a.hpw);       // queries per head per work-group

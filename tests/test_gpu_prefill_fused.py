@@ -9,7 +9,9 @@ one of the other prefill tests.  Cases span local and global layers, the
 clamped-bucket region, windows shorter and longer than R, R = 1 and tiny R,
 d_rel 16 and 32, GQA 1..8 (so 32..256 queries per head and work-group),
 head_dim 64, page sizes 16..128, ragged and empty sequences, and prefill
-over a cached history.
+over a cached history.  Windowed layers with an even GQA run 4-wave
+work-groups (at head_dim 128 with the bias stage in the next K/V buffers),
+odd ones 8-wave work-groups; both are covered.
 """
 import zlib
 
@@ -47,6 +49,10 @@ CASES = [
     ("history-local", spec(4, 2, 128, 512, 512, 64), [700, 1300], [130, 300], 32),
     ("history-global", spec(8, 2, 128, 0, 1024, 64), [2100], [257], 32),
     ("history-one-token", spec(4, 2, 128, 0, 300, 64), [1, 64, 65, 999], [1, 1, 1, 1], 16),
+    ("local-mha-8-waves", spec(3, 3, 128, 256, 256, 64), [600, 257], None, 32),
+    ("local-gqa3-8-waves-p16", spec(6, 2, 128, 300, 300, 16), [500], None, 16),
+    ("local-gqa4-d64-history", spec(8, 2, 64, 128, 128, 64), [400, 700], [64, 333], 32),
+    ("local-gqa2-p256-history", spec(4, 2, 128, 200, 256, 256), [900, 64], [450, 64], 16),
 ]
 
 
@@ -70,12 +76,13 @@ def test_prefill_fused_parity(cid, sp, keys, new, d_rel):
     assert np.max(np.abs(diff), initial=0.0) <= LSE_MAX_ABS, cid
 
 
-def test_fused_matches_streamed_bias():
+@pytest.mark.parametrize("W,R", [(0, 1024), (512, 512)])
+def test_fused_matches_streamed_bias(W, R):
     """The fused kernel and the streaming one given the product rounded to bf16
     (formed here in fp32 from the same bf16 r and W) agree closely: both add
     the same bf16 bias, up to a rare product whose fp32 sums round apart."""
     dev = device()
-    sp = spec(8, 2, 128, 0, 1024, 64)
+    sp = spec(8, 2, 128, W, R, 64)
     case = ri.make_projected(sp, [1500, 777], None, 32, seed=61, device=dev)
     h = case.hist
     bias = torch.matmul(case.rel_r.float(), case.w_rel.float()).to(torch.bfloat16)
