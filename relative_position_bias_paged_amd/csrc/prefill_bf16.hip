@@ -132,6 +132,8 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
 // s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8) that waits for LDS and scalar memory traffic only.
 constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
+// ... and the one that also waits for all vector memory traffic
+constexpr unsigned waitcnt_vm0_lgkm0 = 7u << 4;
 
 // Fused stage layout: two parts of 16 query rows.  Row r of a part starts at
 // element 32 + 104*r and holds distance index e (0..63 in use) at +e.  The
@@ -146,6 +148,14 @@ constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
 // head_dim 128, the wave's own 4 KiB slices of the next K and V buffers,
 // which are free until the wave issues its loads of the next tile.
 constexpr int FUSED_ROW = 104;
+
+// Which matrices of a K/V tile a load issues, and which of the wave's writes
+// (J < 0: all of them).
+template <bool K, bool V, int J>
+struct KVSel {
+  static constexpr bool k = K, v = V;
+  static constexpr int j = J;
+};
 // chunk swizzle of W^T row r in the fused variant's LDS buffers: rows are
 // 2*DR bytes, 128/DR of them fill the 64 banks, so the swizzle steps once
 // per that many rows
@@ -374,7 +384,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const char *k_head = reinterpret_cast<const char *>(kp + (size_t)kvh * head_stride);
   const long long v_minus_k = reinterpret_cast<const char *>(vp) - reinterpret_cast<const char *>(kp);
   const uint32_t page_bytes = (uint32_t)(page_stride * 2);   // checked on the host to fit
-  auto load_kv = [&](int s0, int page_v, uint16_t *kl, uint16_t *vl) {
+  // (sel_tag: which matrices and writes, a KVSel, known at compile time.)
+  auto load_kv_sel = [&](auto sel_tag, int s0, int page_v, uint16_t *kl, uint16_t *vl) {
+    using SEL = decltype(sel_tag);
     // Rows below `first` repeat the work-group's first visible key, rows
     // above `last` the sequence's last key: only keys some query of the
     // work-group sees are ever read (a 0 probability times a finite value is
@@ -388,24 +400,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const char *vt = kt + v_minus_k;
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        if (SEL::j >= 0 && j != SEL::j) continue;
         const uint32_t ro = (uint32_t)min(max(dma_row[j], first), last) * (D * 2);
-        lds_void_t *kd = (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512);
-        lds_void_t *vd = (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512);
-        dma16(kt + (ro + k_off[j]), kd);
-        dma16(vt + (ro + v_off[j]), vd);
+        if constexpr (SEL::k) dma16(kt + (ro + k_off[j]), (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512));
+        if constexpr (SEL::v) dma16(vt + (ro + v_off[j]), (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        if (SEL::j >= 0 && j != SEL::j) continue;
         const int sk = s0 + min(max(dma_row[j], first), last);
         const size_t ko = ((size_t)trow[sk >> lp] * page_stride + (size_t)kvh * head_stride +
                            (size_t)(sk & (P - 1)) * D) * 2;
-        lds_void_t *kd = (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512);
-        lds_void_t *vd = (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512);
-        dma16(reinterpret_cast<const char *>(kp) + ko + k_off[j], kd);
-        dma16(reinterpret_cast<const char *>(vp) + ko + v_off[j], vd);
+        if constexpr (SEL::k)
+          dma16(reinterpret_cast<const char *>(kp) + ko + k_off[j], (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512));
+        if constexpr (SEL::v)
+          dma16(reinterpret_cast<const char *>(vp) + ko + v_off[j], (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512));
       }
     }
+  };
+
+  auto load_kv = [&](int s0, int page_v, uint16_t *kl, uint16_t *vl) {
+    load_kv_sel(KVSel<true, true, -1>{}, s0, page_v, kl, vl);
   };
 
   // ---- bias runs ---------------------------------------------------------
@@ -559,6 +575,91 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int vsw = v_swizzle<D>(vrow);                   // rows ks*16+vrow(+4) share it
   const int vbase = vrow * D + (vi & 1) * 4;
 
+  // S^T block of keys 32*sub .. 32*sub+31 of the K tile at kl (8 MFMAs over
+  // head_dim).
+  auto s_block = [&](const uint16_t *kl, int sub) {
+    f32x16_t acc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = 0.f;
+    const uint16_t *kb0 = kl + kbase + sub * 32 * D;
+    u32x4_t kf[2];
+    kf[0] = *reinterpret_cast<const u32x4_t *>(kb0 + (kx * 8));
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb + 1 < KB)
+        kf[(kb + 1) & 1] = *reinterpret_cast<const u32x4_t *>(kb0 + (((2 * (kb + 1)) ^ kx) * 8));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb & 1]),
+                                                    __builtin_bit_cast(bf16x8_t, qf[kb]), acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  auto max16 = [&](const f32x16_t &acc) {
+    // a chain of two-input maxes, which the compiler fuses into v_max3
+    float m = fmaxf(acc[0], acc[1]);
+#pragma unroll
+    for (int j = 2; j < 16; j += 2) m = fmaxf(fmaxf(m, acc[j]), acc[j + 1]);
+    return m;
+  };
+  // P = exp2(score - max) in bf16, as the PV MFMA consumes it; the row sum
+  // adds exactly these rounded values, two per v_dot2 against (1, 1).
+  // (sa: the exp2 argument's multiplier, c2 its offset)
+  auto probs = [&](f32x16_t &acc, float sa, float c2, u32x4_t (&pw)[2]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_exp2f(fmaf(acc[j], sa, c2));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pw[j >> 2][j & 3] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // (bit_cast of a vector element lvalue reads element 0: copy it out first)
+      const uint32_t w0 = pw[0][j], w1 = pw[1][j];
+      r0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), one2, r0, false);
+      r1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), one2, r1, false);
+    }
+    lsum += r0 + r1;
+  };
+  // O^T += V^T P^T over keys 32*sub .. 32*sub+31 of the V tile at vl, 16 keys
+  // per MFMA.  k-slots of lane half `half` in step ks are keys ks*16 + 8*half
+  // + 0..7: exactly S^T registers 8*(ks&1) + 0..7, and exactly the keys the
+  // two transposing reads deliver.
+  auto pv_block = [&](const uint16_t *vl, const u32x4_t (&pw)[2], int sub) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int ks = 2 * sub + kh;
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw[kh]);
+#pragma unroll
+      for (int ds = 0; ds < DSUB; ++ds) {
+        const uint16_t *v0 = vl + vbase + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0 + 4 * D));
+        const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+        const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], hw[0], hw[1]});
+        oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pb, oacc[ds], 0, 0, 0);
+      }
+    }
+  };
+
+  // Lazy rescale, decided per lane on its own 32 scores: while neither lane
+  // of a pair sees a score above m2 + TAU the shared m2 stands, with no
+  // exchange; otherwise the pair's maximum is formed and both lanes move
+  // m2 to it (mt2: this lane's tile maximum in log2 units).
+  auto rescale = [&](float mt2) {
+    if (__ballot(mt2 > m2 + TAU)) {
+      const float mtp = fmaxf(mt2, __shfl_xor(mt2, 32));
+      const bool exceed = mtp > m2 + TAU;
+      const float mnew = exceed ? mtp : m2;
+      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < DSUB; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
+      m2 = mnew;
+    }
+  };
+
   // fixed_tag: std::integral_constant<bool, true> on tiles known (for the
   // whole work-group) to be clamp-only and unmasked, which then compile to
   // score path 0 with no classification, bias or mask code at all.
@@ -583,26 +684,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     // koff = 32*sub + 16*(j>>3) + (j&7), at distance dq - koff.
     const int dq = p - s0 - 8 * half;
 
-    const uint16_t *kt = kl + kbase;
-    const uint16_t *vt = vl + vbase;
-
-    // S^T block of keys 32*sub .. 32*sub+31 (8 MFMAs over head_dim).
-    auto s_block = [&](int sub) {
-      f32x16_t acc;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = 0.f;
-      const uint16_t *kb0 = kt + sub * 32 * D;
-      u32x4_t kf[2];
-      kf[0] = *reinterpret_cast<const u32x4_t *>(kb0 + (kx * 8));
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB)
-          kf[(kb + 1) & 1] = *reinterpret_cast<const u32x4_t *>(kb0 + (((2 * (kb + 1)) ^ kx) * 8));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[kb & 1]),
-                                                      __builtin_bit_cast(bf16x8_t, qf[kb]), acc, 0, 0, 0);
-      }
-      return acc;
-    };
     // Finished scores of a block on paths 1 and 2 (path 0 keeps the raw q.k).
     auto finish = [&](f32x16_t &acc, int sub) {
       if (path == 1) {
@@ -634,85 +715,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         }
       }
     };
-    auto max16 = [&](const f32x16_t &acc) {
-      // a chain of two-input maxes, which the compiler fuses into v_max3
-      float m = fmaxf(acc[0], acc[1]);
-#pragma unroll
-      for (int j = 2; j < 16; j += 2) m = fmaxf(fmaxf(m, acc[j]), acc[j + 1]);
-      return m;
-    };
-    // P = exp2(score - max) in bf16, as the PV MFMA consumes it; the row sum
-    // adds exactly these rounded values, two per v_dot2 against (1, 1).
-    auto probs = [&](f32x16_t &acc, float c2, u32x4_t (&pw)[2]) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_exp2f(fmaf(acc[j], sa, c2));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pw[j >> 2][j & 3] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-      float r0 = 0.f, r1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // (bit_cast of a vector element lvalue reads element 0: copy it out first)
-        const uint32_t w0 = pw[0][j], w1 = pw[1][j];
-        r0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0), one2, r0, false);
-        r1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1), one2, r1, false);
-      }
-      lsum += r0 + r1;
-    };
-    // O^T += V^T P^T over keys 32*sub .. 32*sub+31, 16 keys per MFMA.  k-slots
-    // of lane half `half` in step ks are keys ks*16 + 8*half + 0..7: exactly
-    // S^T registers 8*(ks&1) + 0..7, and exactly the keys the two transposing
-    // reads deliver.
-    auto pv_block = [&](const u32x4_t (&pw)[2], int sub) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int ks = 2 * sub + kh;
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw[kh]);
-#pragma unroll
-        for (int ds = 0; ds < DSUB; ++ds) {
-          const uint16_t *v0 = vt + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0 + 4 * D));
-          const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
-          const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
-          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, u32x4_t{lw[0], lw[1], hw[0], hw[1]});
-          oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pb, oacc[ds], 0, 0, 0);
-        }
-      }
-    };
 
-    // The two 32-key blocks are software-pipelined so that MFMA work of one
-    // block is in flight while the VALU works on the other: block 1's S^T
-    // MFMAs run during block 0's score finishing, block 0's PV MFMAs during
-    // block 1's exponentials.  The running max is updated once per tile.
-    f32x16_t sa0 = s_block(0);
-    f32x16_t sa1 = s_block(1);
+    // Both S^T blocks, then both blocks' scores, exponentials and P V.  (A
+    // wave's own MFMAs and vector instructions do not run side by side; the
+    // two waves of a SIMD overlap each other's.)  The running max is updated
+    // once per tile.
+    f32x16_t sa0 = s_block(kl, 0);
+    f32x16_t sa1 = s_block(kl, 1);
     finish(sa0, 0);
     const float mx0 = max16(sa0);
     finish(sa1, 1);
-    // Lazy rescale, decided per lane on its own 32 scores: while neither lane
-    // of a pair sees a score above m2 + TAU the shared m2 stands, with no
-    // exchange; otherwise the pair's maximum is formed and both lanes move
-    // m2 to it.
-    const float mt2 = fmaf(fmaxf(mx0, max16(sa1)), sa, sb);
-    if (__ballot(mt2 > m2 + TAU)) {
-      const float mtp = fmaxf(mt2, __shfl_xor(mt2, 32));
-      const bool exceed = mtp > m2 + TAU;
-      const float mnew = exceed ? mtp : m2;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < DSUB; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
-      m2 = mnew;
-    }
+    rescale(fmaf(fmaxf(mx0, max16(sa1)), sa, sb));
     const float c2 = sb - m2;
     u32x4_t pw0[2], pw1[2];
-    probs(sa0, c2, pw0);
-    pv_block(pw0, 0);
-    probs(sa1, c2, pw1);
-    pv_block(pw1, 1);
+    probs(sa0, sa, c2, pw0);
+    pv_block(vl, pw0, 0);
+    probs(sa1, sa, c2, pw1);
+    pv_block(vl, pw1, 1);
   };
 
   // ---- main loop -------------------------------------------------------------
@@ -724,7 +743,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     return in_range(s0, band_lo, band_span);
   };
 
-  u32x4_t bias_r[4] = {zero4, zero4, zero4, zero4};
+  // bias runs of the current tile (in 8-wave work-groups set before the
+  // first general step, so that they are not live across the two-group
+  // phase below)
+  u32x4_t bias_r[4];
+  auto clear_bias_r = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bias_r[i] = zero4;
+  };
+  if constexpr (NW != 8) clear_bias_r();
   // Page of tile s (0 past the last tile, where it is not used).  The index
   // carries an opaque zero so the value stays in a vector register until
   // load_kv reads it, instead of being moved to a scalar register (and
@@ -813,15 +840,231 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int lim = min(P0 - (BN - 2) - R, n_k - BN);
     n_fixed = lim < 0 ? 0 : min(lim / BN + 1, n_t - 1);
   }
-  int i_fixed = 0;
-  for (; i_fixed + 2 <= n_fixed; i_fixed += 2) {
-    step(FixedTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt);
-    step(FixedTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
-  }
   bool go = true;
-  if (i_fixed < n_fixed) {   // an odd count: the general loop starts on buffer 1
-    step(FixedTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt);
-    go = step(AnyTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
+  if constexpr (NW == 8) {
+    if (n_fixed > 0) {
+      // Two wave groups in opposite phases.  A SIMD runs one wave's matrix
+      // instructions beside another wave's vector instructions, but not
+      // beside its own, and waves w and w+4 share a SIMD.  Every wave runs
+      // M(j) (P V of tile j-1, then S^T of tile j: matrix work), a barrier,
+      // V(j) (the probabilities of tile j: vector work), a barrier, for
+      // j = 0, 1, ...; the lead group (waves 0-3) starts one barrier ahead,
+      // so its M(j) runs in phase 2j beside the other group's V(j-1), and
+      // its V(j) in phase 2j+1 beside the other group's M(j).  A wave's
+      // arithmetic is that of the one-phase step, in the same order.
+      // K(j) is read in phases 2j and 2j+1, V(j) in 2j+2 and 2j+3.  In phase
+      // 2j every wave issues its slices of K(j+1) and V(j), into the buffers
+      // that K(j-1) and V(j-2) last used in phase 2j-1; they are waited for
+      // at the end of phase 2j+1.  A wave's direct loads stall its issue
+      // while the memory pipeline is busy, so each wave spreads its loads
+      // through its phase: the lead group between its MFMAs, the other
+      // between the steps of its vector work.
+      const int n = n_fixed;
+      const bool lead = wave < 4;
+      const float sb0 = b_last * LOG2E;
+      f32x16_t ps0, ps1;                // S^T of a tile, from its M to its V
+      u32x4_t pp0[2], pp1[2];           // its P, from its V to the next M
+      // Loads of phase 2t: K(t+1) while t < n with the page in pk, V(t) from
+      // t = 1 (V(0) came with K(0)) with the page in pv.
+      auto pp_dma = [&](int t, uint16_t *kn, uint16_t *vc, int pv, int pk) {
+        if (t < n) load_kv_sel(KVSel<true, false, -1>{}, (t + 1) * BN, pk, kn, kn);
+        if (t > 0) load_kv_sel(KVSel<false, true, -1>{}, t * BN, pv, vc, vc);
+      };
+      // The rest of phase 2t's loads: at t = n each wave's bias stage or W^T
+      // rows of tile t; then pv takes the page of tile t+2, so the two page
+      // registers swap roles from one tile to the next.
+      auto pp_load_end = [&](int t, uint16_t *wn, int &pv) {
+        if (t == n) {
+          if constexpr (FUSED) {
+            if (wg_band(t * BN)) load_wslice(t * BN, wn);
+          } else if (use_stage && wave_band(t * BN)) {
+            stage_bias(t * BN);
+          }
+        }
+        pv = tile_page(min(t + 2, n_t - 1) * BN);
+      };
+      auto pp_load = [&](int t, uint16_t *kn, uint16_t *vc, uint16_t *wn, int &pv, int &pk) {
+        pp_dma(t, kn, vc, pv, pk);
+        pp_load_end(t, wn, pv);
+      };
+      // End of a phase: this wave's LDS reads, and at the end of odd phases
+      // its direct loads, are done.  No fence: a release fence would also
+      // wait for the loads left in flight across even phases; the empty asm
+      // keeps the compiler from moving memory accesses across the barrier,
+      // and the scheduling barriers keep each phase's arithmetic in it (the
+      // scheduler would otherwise sink the exponentials into the next phase,
+      // beside the same wave's MFMAs).
+      auto pp_barrier = [&](auto loads_tag) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        if constexpr (decltype(loads_tag)::value) __builtin_amdgcn_s_waitcnt(waitcnt_vm0_lgkm0);
+        else __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      const std::true_type waits{};       // end of an odd phase: loads done too
+      const std::false_type no_wait{};
+      // M: MFMAs i0 .. i1-1 of the stream P V of the tile in vp (0 .. NPV-1:
+      // block sub, k-step kh, slab ds), then S^T of the tile in kc (NPV ..
+      // NM-1: k-step kb, block sub, the two blocks' chains interleaved), each
+      // LDS operand read three MFMAs ahead.  The order of the MFMAs into each
+      // accumulator is that of pv_block and s_block.
+      constexpr int NPV = 2 * 2 * DSUB, NM = NPV + 2 * KB;
+      auto pp_m = [&](const uint16_t *vp, const uint16_t *kc, int i0, int i1, auto hook) {
+        auto rd = [&](int i) {
+          if (i < NPV) {
+            const int ks = 2 * (i / (2 * DSUB)) + (i / DSUB) % 2, ds = i % DSUB;
+            const uint16_t *v0 = vp + vbase + ks * 16 * D + (((ds * 4) | vchunk_lo) ^ vsw) * 8;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(v0 + 4 * D));
+            const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo);
+            const u32x2_t hw = __builtin_bit_cast(u32x2_t, hi);
+            return u32x4_t{lw[0], lw[1], hw[0], hw[1]};
+          }
+          const int sub = (i - NPV) & 1, kb = (i - NPV) >> 1;
+          return *reinterpret_cast<const u32x4_t *>(kc + kbase + sub * 32 * D + (((2 * kb) ^ kx) * 8));
+        };
+        auto mf = [&](int i, const u32x4_t &op) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, op);
+          if (i < NPV) {
+            const int kh = (i / DSUB) % 2, ds = i % DSUB;
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, (i / (2 * DSUB)) ? pp1[kh] : pp0[kh]);
+            oacc[ds] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[ds], 0, 0, 0);
+          } else {
+            const int kb = (i - NPV) >> 1;
+            f32x16_t &acc = ((i - NPV) & 1) ? ps1 : ps0;
+            if (kb == 0) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+            }
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8_t, qf[kb]), acc, 0, 0, 0);
+          }
+        };
+        constexpr int AHEAD = 3;
+        u32x4_t ob[AHEAD + 1];
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i)
+          if (i0 + i < i1) ob[(i0 + i) % (AHEAD + 1)] = rd(i0 + i);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          if (i >= i0 && i < i1) {
+            if (i + AHEAD < i1) ob[(i + AHEAD) % (AHEAD + 1)] = rd(i + AHEAD);
+            mf(i, ob[i % (AHEAD + 1)]);
+            hook(i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      };
+      // V: the probabilities of the tile, hook(q) between its steps (the
+      // scheduling barriers keep loads issued there spread through it)
+      auto pp_v = [&](auto hook) {
+        hook(0);
+        __builtin_amdgcn_sched_barrier(0);
+        rescale(fmaf(fmaxf(max16(ps0), max16(ps1)), scale2, sb0));
+        float c2 = sb0 - m2;
+        asm volatile("" : "+v"(c2));
+        hook(1);
+        __builtin_amdgcn_sched_barrier(0);
+        probs(ps0, scale2, c2, pp0);
+        {
+          u32x4_t q0 = pp0[0], q1 = pp0[1];
+          asm volatile("" : "+v"(q0), "+v"(q1));
+          pp0[0] = q0, pp0[1] = q1;
+        }
+        hook(2);
+        __builtin_amdgcn_sched_barrier(0);
+        probs(ps1, scale2, c2, pp1);
+        hook(3);
+        // formed here, not after the wait that ends the phase (through
+        // locals: the asm may not name the kernel's variables here)
+        u32x4_t q0 = pp0[0], q1 = pp0[1], q2 = pp1[0], q3 = pp1[1];
+        float ls = lsum;
+        asm volatile("" : "+v"(q0), "+v"(q1), "+v"(q2), "+v"(q3), "+v"(ls));
+        pp0[0] = q0, pp0[1] = q1, pp1[0] = q2, pp1[1] = q3, lsum = ls;
+      };
+      // Each group runs its own copy of the phase sequence, so that every wait
+      // in it is known at compile time.
+      auto pp_run = [&](auto lead_tag, int &pa, int &pb) {
+        constexpr bool LEAD = decltype(lead_tag)::value;
+        auto no_hook = [](int) {};
+        // Tile j (0 < j < n): K(j) in kc, V(j-1) in vp; the loads of phase 2j
+        // (lead: after the LDS reads of M(j)) and 2j+2 (others: before V(j))
+        // go to kn/vc and kc/vp.  pa holds the page of tile j, pb that of
+        // tile j+1.
+        auto pp_tile = [&](int j, uint16_t *kc, uint16_t *kn, uint16_t *vc, uint16_t *vp, int &pa,
+                           int &pb) {
+          pp_m(vp, kc, 0, NM, no_hook);
+          if constexpr (LEAD) {
+            pp_load(j, kn, vc, nullptr, pa, pb);
+            pp_barrier(no_wait);
+            pp_v(no_hook);
+            pp_barrier(waits);
+          } else {
+            pp_barrier(waits);
+            pp_load(j + 1, kc, vp, (j & 1) ? wsl0 : wsl1, pb, pa);
+            pp_v(no_hook);
+            pp_barrier(no_wait);
+          }
+        };
+        // tile 0: no P V before its S^T; the other group starts one barrier later
+        if constexpr (!LEAD) {
+          pp_load(0, k_lds1, v_lds0, nullptr, pa, pb);
+          pp_barrier(no_wait);
+        }
+        pp_m(nullptr, k_lds0, NPV, NM, no_hook);
+        if constexpr (LEAD) {
+          pp_load(0, k_lds1, v_lds0, nullptr, pa, pb);
+          pp_barrier(no_wait);
+        } else {
+          pp_barrier(waits);
+          pp_load(1, k_lds0, v_lds1, (n == 1) ? wsl1 : nullptr, pb, pa);
+        }
+        pp_v(no_hook);
+        if constexpr (LEAD) pp_barrier(waits);
+        else pp_barrier(no_wait);
+        int j = 1;
+        for (; j + 2 <= n; j += 2) {
+          pp_tile(j, k_lds1, k_lds0, v_lds1, v_lds0, pb, pa);
+          pp_tile(j + 1, k_lds0, k_lds1, v_lds0, v_lds1, pa, pb);
+        }
+        if (j < n) pp_tile(j, k_lds1, k_lds0, v_lds1, v_lds0, pb, pa);
+        // j = n: P V of tile n-1, with the lead's loads of phase 2n (the other
+        // group skips its last barrier: its phases end one barrier later)
+        pp_m((n & 1) ? v_lds0 : v_lds1, nullptr, 0, NPV, no_hook);
+        if constexpr (LEAD) {
+          pp_load(n, (n & 1) ? k_lds0 : k_lds1, (n & 1) ? v_lds1 : v_lds0, (n & 1) ? wsl1 : wsl0,
+                  (n & 1) ? pb : pa, (n & 1) ? pa : pb);
+          pp_barrier(no_wait);
+        }
+        pp_barrier(waits);
+      };
+      int pa = 0, pb = page_nxt;
+      if (lead) pp_run(std::true_type{}, pa, pb);
+      else pp_run(std::false_type{}, pa, pb);
+      // page of tile n+1 for the general loop
+      int &pg_n1 = (n & 1) ? pa : pb;
+      page_nxt = pg_n1;
+      // the general loop goes on from tile n_fixed, in buffer n_fixed % 2
+      clear_bias_r();
+      s_cur = n_fixed * BN;
+      s_nxt = tile_after(s_cur);
+      s_nxt2 = tile_after(s_nxt);
+      steps_left = n_t - n_fixed;
+      if (n_fixed & 1) go = step(AnyTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
+    } else {
+      clear_bias_r();
+    }
+  } else {
+    int i_fixed = 0;
+    for (; i_fixed + 2 <= n_fixed; i_fixed += 2) {
+      step(FixedTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt);
+      step(FixedTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
+    }
+    if (i_fixed < n_fixed) {   // an odd count: the general loop starts on buffer 1
+      step(FixedTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt);
+      go = step(AnyTile{}, k_lds1, v_lds1, k_lds0, v_lds0, wsl1, wsl0, page_nxt);
+    }
   }
   while (go) {
     if (!step(AnyTile{}, k_lds0, v_lds0, k_lds1, v_lds1, wsl0, wsl1, page_nxt)) break;

@@ -15,7 +15,7 @@ import torch
 
 import rba_inputs as ri
 from gpu_helpers import (LSE_MAX_ABS, assert_parity, device, errors, gpu_prefill,
-                         oracle_prefill, sample_positions)
+                         oracle_prefill, oracle_prefill_history, sample_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +155,44 @@ def test_gqa_equals_repeated_mha(W, R):
         max_abs, mean_rel = errors(o_mha, o_gqa.double().cpu().numpy())
         assert max_abs <= 2e-2 and mean_rel <= 5e-3
     assert_parity(o_mha, oracle_prefill(case), sp.dtype, "MHA twin")
+
+
+# Global layers: lengths and extents give each work-group shape a different
+# count of leading clamp-only tiles (odd and even), page sizes below, at and
+# above the 64-key tile, head_dim 64 and 128, GQA 2..8, and a cached history.
+CLAMP_ONLY_CASES = [
+    ("r64-p64", spec(8, 2, 128, 0, 64, 64), [1000, 65, 700, 129], None),
+    ("r100-p16", spec(8, 2, 128, 0, 100, 16), [513, 300, 64], None),
+    ("d64-r32-p32", spec(4, 1, 64, 0, 32, 32), [900, 257], None),
+    ("gqa8-r128-p128", spec(16, 2, 128, 0, 128, 128), [2000], None),
+    ("history-r64", spec(8, 2, 128, 0, 64, 64), [1500, 700], [333, 64]),
+]
+
+
+@pytest.mark.parametrize("cid,sp,lens,new", CLAMP_ONLY_CASES, ids=[c[0] for c in CLAMP_ONLY_CASES])
+def test_clamp_only_tiles_bit_exact_across_groupings(cid, sp, lens, new):
+    """On a global layer the leading tiles that are clamp-only for the whole
+    work-group run in a phase of their own, whose length depends on the
+    work-group's first query and so on the head grouping; the tiles after it
+    run the general step.  GQA against MHA over a repeated pool moves tiles
+    between the two, and the rows stay bit-identical (each wave's arithmetic
+    is the same in both); both meet the oracle."""
+    dev = device()
+    seed = zlib.crc32(cid.encode()) % 100000
+    if new is None:
+        case = ri.make_prefill(sp, lens, seed=seed, device=dev,
+                               num_pages=sum(-(-n // sp.page_size) for n in lens) + 3)
+    else:
+        case = ri.make_prefill_history(sp, lens, new, seed=seed, device=dev)
+    G = sp.num_q_heads // sp.num_kv_heads
+    k_mha = case.k_pool.repeat_interleave(G, dim=1).contiguous()
+    v_mha = case.v_pool.repeat_interleave(G, dim=1).contiguous()
+    o_gqa = gpu_prefill(case)
+    o_mha = gpu_prefill(case, k_pool=k_mha, v_pool=v_mha)
+    torch.cuda.synchronize()
+    assert torch.equal(o_gqa.view(torch.int16), o_mha.view(torch.int16))
+    ref = oracle_prefill(case) if new is None else oracle_prefill_history(case)
+    assert_parity(o_gqa, ref, sp.dtype, cid)
 
 
 @pytest.mark.parametrize("R", [64, 1024])
