@@ -1,8 +1,9 @@
 """Window-only local pools: each sequence owns a ring of
 rba_window_ring_pages(window, page_size, max_new) pages, and its positional
 block table maps page j to ring[j % ring_pages].  Keys older than the window
-are overwritten as the sequence grows; the kernels never read them (nor the
-ring slots no query of a call sees, whatever they hold).
+are overwritten as the sequence grows; no output depends on them (nor on
+the ring slots no query of a call sees, whatever they hold): prefill never
+loads them, decode loads the pages that hold them and masks them out.
 
 Checked on the GPU against the oracle on the full logical keys: a local
 layer prefilled chunk by chunk (append, then prefill over the history) into
