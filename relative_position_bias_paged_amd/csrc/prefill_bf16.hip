@@ -129,6 +129,18 @@ __device__ __forceinline__ void dma16(const void *src, lds_void_t *lds) {
   __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
+// The same through a buffer resource (base and byte count uniform, lane l's
+// 16 bytes at base + voff, zeros past the count).  While a load of the global
+// form is in flight the compiler waits for every LDS read to complete before
+// using any of them; with the buffer form it keeps partial waits.
+constexpr int BUF_WORD3 = 0x00020000;   // resource word 3: 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, BUF_WORD3);
+}
+__device__ __forceinline__ void buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, lds_void_t *lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+
 // s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8) that waits for LDS and scalar memory traffic only.
 constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
@@ -398,12 +410,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       const uint32_t page = (uint32_t)__builtin_amdgcn_readfirstlane(page_v);
       const char *kt = k_head + ((uint64_t)page * page_bytes + (uint32_t)((s0 & (P - 1)) * D * 2));
       const char *vt = kt + v_minus_k;
+      // resources over the tile's BN rows
+      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kt, BN * D * 2), rv = buf_rsrc(vt, BN * D * 2);
 #pragma unroll
       for (int j = 0; j < DMA_PER_WAVE; ++j) {
         if (SEL::j >= 0 && j != SEL::j) continue;
         const uint32_t ro = (uint32_t)min(max(dma_row[j], first), last) * (D * 2);
-        if constexpr (SEL::k) dma16(kt + (ro + k_off[j]), (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512));
-        if constexpr (SEL::v) dma16(vt + (ro + v_off[j]), (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512));
+        if constexpr (SEL::k) buf16(rk, ro + k_off[j], (lds_void_t *)(kl + (DMA_PER_WAVE * wave + j) * 512));
+        if constexpr (SEL::v) buf16(rv, ro + v_off[j], (lds_void_t *)(vl + (DMA_PER_WAVE * wave + j) * 512));
       }
     } else {
 #pragma unroll
@@ -443,21 +457,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   const int fw_off = 32 + (FUSED_ROW - 1) * frow - (ALIAS ? 16 * (col >> 4) : 0) + 4 * half;
   const int fr_off = 32 + FUSED_ROW * frow;
   // Stage write k of this lane: row 8k + lane/8 of the wave, physical chunk
-  // lane%8 = logical chunk c ^ swizzle.  Pointer for tile 0; tile s0 is
-  // s0 elements lower.
-  const char *sptr[4];
+  // lane%8 = logical chunk c ^ swizzle.  The loads go through a resource
+  // over the wave's 32 bias rows, from 128 elements before its first row (a
+  // wave wholly past the sequence takes the sequence's last row instead, so
+  // the resource never starts past the tensor); sofs is the byte offset of
+  // tile 0, tile s0 is s0 elements lower.  A staged distance is at least -94,
+  // so every offset stays above 68 bytes, and at most R + 100 elements past
+  // its row start.  Rows of queries past the sequence get an offset of at
+  // least 2^31 for every tile (positions stay below 2^29), beyond the record
+  // count: the hardware returns zeros for them without a memory access, and
+  // their outputs are never stored.
+  const int tq_base = min(tq0, L - 1);
+  const size_t srow0 = ((size_t)tok0 + tq_base) * Hq + h;
+  const __amdgpu_buffer_rsrc_t rstage = buf_rsrc(
+      static_cast<const uint16_t *>(a.bias) + ((long long)srow0 * R - 128),
+      (int)min(((long long)31 * Hq * R + R + 256) * 2, (long long)INT_MAX));
+  uint32_t sofs[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int rq = 8 * k + (lane >> 3);
     const int tq = tq0 + rq;
     const int c = (lane & 7) ^ ((rq >> 1) & 7);
-    const size_t rrow = ((size_t)tok0 + (tq < L ? tq : 0)) * Hq + h;
-    sptr[k] = reinterpret_cast<const char *>(static_cast<const uint16_t *>(a.bias) + rrow * R) +
-              2 * (long long)(hist + tq - (BN - 1) + 8 * c);
+    sofs[k] = (tq < L) ? (uint32_t)((((long long)(tq - tq_base) * Hq) * R + 128 + hist + tq - (BN - 1) + 8 * c) * 2)
+                       : 0xC0000000u;
   }
   auto stage_bias = [&](int s0) {       // direct loads, tile s0 -> this wave's stage
 #pragma unroll
-    for (int k = 0; k < 4; ++k) dma16(sptr[k] - 2 * (long long)s0, (lds_void_t *)(stage_w + k * 512));
+    for (int k = 0; k < 4; ++k) buf16(rstage, sofs[k] - 2 * (uint32_t)s0, (lds_void_t *)(stage_w + k * 512));
   };
   auto load_bias = [&](int s0, u32x4_t (&bp)[4], const uint16_t *part) {
     if constexpr (FUSED) {
@@ -498,14 +524,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     if constexpr (FUSED) {
       constexpr int LPR = DR / 8;        // lanes per W^T row (16 bytes each)
       constexpr int RPI = 64 / LPR;      // rows per 1 KiB direct load
-      const uint16_t *wt = static_cast<const uint16_t *>(a.w_rel_t);
+      const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.w_rel_t, R * DR * 2);
       const int n_ld = (QM + 64) / RPI;
       const int d0 = P0 - s0 - (BN - 1);
       for (int i = wave; i < n_ld; i += NW) {
         const int rr = i * RPI + lane / LPR;                 // buffer row this lane fills
         const int dd = min(max(d0 + rr, 0), R - 1);
         const int c = (lane % LPR) ^ wsl_swizzle<DR>(rr);    // logical chunk it fetches
-        dma16(wt + (size_t)dd * DR + c * 8, (lds_void_t *)(dst + i * 512));
+        buf16(rw, (uint32_t)((dd * DR + c * 8) * 2), (lds_void_t *)(dst + i * 512));
       }
     }
   };
@@ -873,8 +899,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       // The rest of phase 2t's loads: at t = n each wave's bias stage or W^T
       // rows of tile t; then pv takes the page of tile t+2, so the two page
       // registers swap roles from one tile to the next.
-      auto pp_load_end = [&](int t, uint16_t *wn, int &pv) {
-        if (t == n) {
+      // (last_tag: t = n is known to hold, false, or to be tested, a
+      // std::integral_constant<int, 1, 0 or -1>)
+      auto pp_load_end = [&](auto last_tag, int t, uint16_t *wn, int &pv) {
+        constexpr int LAST = decltype(last_tag)::value;
+        if (LAST == 1 || (LAST < 0 && t == n)) {
           if constexpr (FUSED) {
             if (wg_band(t * BN)) load_wslice(t * BN, wn);
           } else if (use_stage && wave_band(t * BN)) {
@@ -883,10 +912,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         }
         pv = tile_page(min(t + 2, n_t - 1) * BN);
       };
-      auto pp_load = [&](int t, uint16_t *kn, uint16_t *vc, uint16_t *wn, int &pv, int &pk) {
+      auto pp_load = [&](auto last_tag, int t, uint16_t *kn, uint16_t *vc, uint16_t *wn, int &pv, int &pk) {
         pp_dma(t, kn, vc, pv, pk);
-        pp_load_end(t, wn, pv);
+        pp_load_end(last_tag, t, wn, pv);
       };
+      const std::integral_constant<int, 1> is_last{};
+      const std::integral_constant<int, 0> not_last{};
+      const std::integral_constant<int, -1> maybe_last{};
       // End of a phase: this wave's LDS reads, and at the end of odd phases
       // its direct loads, are done.  No fence: a release fence would also
       // wait for the loads left in flight across even phases; the empty asm
@@ -992,48 +1024,49 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
         // (lead: after the LDS reads of M(j)) and 2j+2 (others: before V(j))
         // go to kn/vc and kc/vp.  pa holds the page of tile j, pb that of
         // tile j+1.
-        auto pp_tile = [&](int j, uint16_t *kc, uint16_t *kn, uint16_t *vc, uint16_t *vp, int &pa,
-                           int &pb) {
+        // (last_tag: whether j + 1 = n, for the other group's loads)
+        auto pp_tile = [&](auto last_tag, int j, uint16_t *kc, uint16_t *kn, uint16_t *vc, uint16_t *vp,
+                           int &pa, int &pb) {
           pp_m(vp, kc, 0, NM, no_hook);
           if constexpr (LEAD) {
-            pp_load(j, kn, vc, nullptr, pa, pb);
+            pp_load(not_last, j, kn, vc, nullptr, pa, pb);
             pp_barrier(no_wait);
             pp_v(no_hook);
             pp_barrier(waits);
           } else {
             pp_barrier(waits);
-            pp_load(j + 1, kc, vp, (j & 1) ? wsl0 : wsl1, pb, pa);
+            pp_load(last_tag, j + 1, kc, vp, (j & 1) ? wsl0 : wsl1, pb, pa);
             pp_v(no_hook);
             pp_barrier(no_wait);
           }
         };
         // tile 0: no P V before its S^T; the other group starts one barrier later
         if constexpr (!LEAD) {
-          pp_load(0, k_lds1, v_lds0, nullptr, pa, pb);
+          pp_load(not_last, 0, k_lds1, v_lds0, nullptr, pa, pb);
           pp_barrier(no_wait);
         }
         pp_m(nullptr, k_lds0, NPV, NM, no_hook);
         if constexpr (LEAD) {
-          pp_load(0, k_lds1, v_lds0, nullptr, pa, pb);
+          pp_load(not_last, 0, k_lds1, v_lds0, nullptr, pa, pb);
           pp_barrier(no_wait);
         } else {
           pp_barrier(waits);
-          pp_load(1, k_lds0, v_lds1, (n == 1) ? wsl1 : nullptr, pb, pa);
+          pp_load(maybe_last, 1, k_lds0, v_lds1, wsl1, pb, pa);
         }
         pp_v(no_hook);
         if constexpr (LEAD) pp_barrier(waits);
         else pp_barrier(no_wait);
         int j = 1;
         for (; j + 2 <= n; j += 2) {
-          pp_tile(j, k_lds1, k_lds0, v_lds1, v_lds0, pb, pa);
-          pp_tile(j + 1, k_lds0, k_lds1, v_lds0, v_lds1, pa, pb);
+          pp_tile(maybe_last, j, k_lds1, k_lds0, v_lds1, v_lds0, pb, pa);
+          pp_tile(maybe_last, j + 1, k_lds0, k_lds1, v_lds0, v_lds1, pa, pb);
         }
-        if (j < n) pp_tile(j, k_lds1, k_lds0, v_lds1, v_lds0, pb, pa);
+        if (j < n) pp_tile(maybe_last, j, k_lds1, k_lds0, v_lds1, v_lds0, pb, pa);
         // j = n: P V of tile n-1, with the lead's loads of phase 2n (the other
         // group skips its last barrier: its phases end one barrier later)
         pp_m((n & 1) ? v_lds0 : v_lds1, nullptr, 0, NPV, no_hook);
         if constexpr (LEAD) {
-          pp_load(n, (n & 1) ? k_lds0 : k_lds1, (n & 1) ? v_lds1 : v_lds0, (n & 1) ? wsl1 : wsl0,
+          pp_load(is_last, n, (n & 1) ? k_lds0 : k_lds1, (n & 1) ? v_lds1 : v_lds0, (n & 1) ? wsl1 : wsl0,
                   (n & 1) ? pb : pa, (n & 1) ? pa : pb);
           pp_barrier(no_wait);
         }

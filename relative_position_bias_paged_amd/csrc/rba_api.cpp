@@ -170,6 +170,8 @@ rba_status prefill_impl(const void *q, const int32_t *cu_seqlens, int32_t total_
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
   if ((long long)max_seqlen > (long long)pt->max_pages_per_seq * pt->page_size)
     return RBA_ERR_INVALID_ARG;
+  // key positions stay below 2^29 (the bias stage's offsets rely on it)
+  if ((long long)pt->max_pages_per_seq * pt->page_size >= (1LL << 29)) return RBA_ERR_UNSUPPORTED;
 
   rba::PrefillArgs a{};
   a.q = q;

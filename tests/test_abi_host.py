@@ -104,6 +104,13 @@ def test_prefill_argument_errors(kwargs):
     assert _prefill(kv, pt, prm, **kwargs) == rba.RBA_ERR_INVALID_ARG
 
 
+def test_prefill_key_positions_below_2_pow_29():
+    # the page table reaches 2^29 keys: refused before any launch
+    kv, pt, prm = _layer(max_pages=1 << 23)
+    assert _prefill(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED
+    assert _prefill_fused(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED
+
+
 def test_prefill_empty_is_noop():
     kv, pt, prm = _layer()
     assert _prefill(kv, pt, prm, q=0, cu=0, bias=0, out=0, T=0) == rba.RBA_OK
