@@ -147,19 +147,24 @@ constexpr unsigned waitcnt_lgkm0 = 0xFu | (7u << 4) | (0u << 8) | (3u << 14);
 // ... and the one that also waits for all vector memory traffic
 constexpr unsigned waitcnt_vm0_lgkm0 = 7u << 4;
 
-// Fused stage layout: two parts of 16 query rows.  Row r of a part starts at
-// element 32 + 104*r and holds distance index e (0..63 in use) at +e.  The
-// product for distance index idx = e + q of query q = 16*hi + r is written at
-// 32 + 103*r - 16*hi + idx of part hi, so a lane's writes sit at fixed offsets
-// from one per-lane base; the indices it also computes outside 0..63
-// (-31..95) land in the unused elements 64..103 of its own or the previous
-// row, or in the part's 32-element head (every write stays in elements
-// 16..1671 of its part).  Rows 208 bytes apart put the 16 rows one aligned
-// 16-byte read serves on distinct banks.  The two parts are either one
-// stage of 32 rows (part 1 = part 0 + 16 rows) or, in 4-wave work-groups over
-// head_dim 128, the wave's own 4 KiB slices of the next K and V buffers,
+// Fused stage layout: two parts of 16 query rows.  Row r of part hi starts at
+// element h1*hi + 32 + 105*r and holds distance index e (0..63 in use) at +e
+// (h1: 28 when the parts are separate slices, below; else 0 with part 1 =
+// part 0 + 16 rows).  The product for distance index idx = e + q of query
+// q = 16*hi + r is written at 32 + 104*r + (h1 - 16)*hi + idx, so a lane's
+// writes sit at fixed offsets from one per-lane base, and its runs of four
+// consecutive indices (idx = 4k .. 4k+3) are 8-byte aligned: one 8-byte store
+// each.  The indices a lane also computes outside 0..63 (-31..95) land in the
+// unused elements 64..104 of its own or the previous row, or in the part's
+// head (writes and reads stay in elements 32..1700 of a separate slice).  A row starts on
+// an odd element when r is odd, so the lanes read their 8-element runs as
+// five 4-byte words and shift out one element.  The pitch and h1 put the
+// 8-byte stores and the 4-byte reads of every half-wave on distinct banks.
+// The two parts are either one stage of 32 rows or, in 4-wave work-groups
+// over head_dim 128, the wave's own 4 KiB slices of the next K and V buffers,
 // which are free until the wave issues its loads of the next tile.
-constexpr int FUSED_ROW = 104;
+constexpr int FUSED_ROW = 105;
+constexpr int FUSED_PART1 = 28;
 
 // Which matrices of a K/V tile a load issues, and which of the wave's writes
 // (J < 0: all of them).
@@ -190,9 +195,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
   constexpr int ROWS_PER_DMA = 512 / D;         // key rows per 1 KiB LDS write
   constexpr int DMA_PER_WAVE = BN * D / 512 / NW;  // 1 KiB writes per wave per matrix
-  // a fused stage part (writes up to element 32 + 15*103 + 4 + 91) fits the
-  // wave's slice of a K or V buffer
-  static_assert(!ALIAS || DMA_PER_WAVE * 512 > 32 + 15 * (FUSED_ROW - 1) + 4 + 91, "stage part too large");
+  // a fused stage part (writes up to element h1 - 16 + 32 + 15*104 + 4 + 95,
+  // reads up to h1 + 32 + 15*105 + 56 + 9) fits the wave's slice of a K or V buffer
+  static_assert(!ALIAS || (DMA_PER_WAVE * 512 > FUSED_PART1 + 32 + 15 * (FUSED_ROW - 1) + 99 &&
+                           DMA_PER_WAVE * 512 > FUSED_PART1 + 32 + 15 * FUSED_ROW + 65),
+                "stage part too large");
+  static_assert(FUSED_ROW % 4 == 1 && FUSED_ROW > 96 && (FUSED_PART1 - 16) % 4 == 0,
+                "fused stage: 8-byte aligned runs of four, rows apart by more than 96");
   // two K/V buffers as separate objects, so the compiler can tell that the
   // direct loads into one do not alias reads of the other
   __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
@@ -454,8 +463,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     else return stage_w;
   };
   const int frow = ALIAS ? (col & 15) : col;
-  const int fw_off = 32 + (FUSED_ROW - 1) * frow - (ALIAS ? 16 * (col >> 4) : 0) + 4 * half;
-  const int fr_off = 32 + FUSED_ROW * frow;
+  const int fw_off = 32 + (FUSED_ROW - 1) * frow + (ALIAS ? (FUSED_PART1 - 16) * (col >> 4) : 0) + 4 * half;
+  const int fr_off = 32 + FUSED_ROW * frow + (ALIAS ? FUSED_PART1 * (col >> 4) : 0);
+  // the row start's element parity: a run is read as five words from the
+  // word holding its first element, shifted right by fr_shift bytes
+  const uint32_t fr_shift = 2u * (uint32_t)(fr_off & 1);
+  const int fr_word = fr_off >> 1;
   // Stage write k of this lane: row 8k + lane/8 of the wave, physical chunk
   // lane%8 = logical chunk c ^ swizzle.  The loads go through a resource
   // over the wave's 32 bias rows, from 128 elements before its first row (a
@@ -489,7 +502,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     if constexpr (FUSED) {
 #pragma unroll
       for (int p = 0; p < 4; ++p)
-        bp[p] = *reinterpret_cast<const u32x4_t *>(part + fr_off + (7 - half - 2 * p) * 8);
+      {
+        const uint32_t *wp = reinterpret_cast<const uint32_t *>(part) + fr_word + (7 - half - 2 * p) * 4;
+        uint32_t w[5];
+#pragma unroll
+        for (int k = 0; k < 5; ++k) w[k] = wp[k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) bp[p][k] = __builtin_amdgcn_alignbyte(w[k + 1], w[k], fr_shift);
+      }
     } else if (use_stage) {
       const int sw = (col >> 1) & 7;
 #pragma unroll
@@ -546,10 +566,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
       // row depends on col only: 32 rows are whole swizzle periods)
       const int wsw = wsl_swizzle<DR>(col);
       const uint16_t *wa = wsl + (32 * qb + col) * DR;
-      // 2-byte stores, kept apart: merged into 8-byte ones they would sit at
-      // 2-byte-aligned addresses, which LDS serves with long stalls
-      typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
-      volatile lds_u16_t *sb = (volatile lds_u16_t *)(part + fw_off);
+      // 8-byte stores of four consecutive indices (8-byte aligned)
+      typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+      lds_u32x2_t *sb = (lds_u32x2_t *)(part + fw_off);
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         f32x16_t acc;
@@ -562,13 +581,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
                                                         __builtin_bit_cast(bf16x8_t, rf[kk]), acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; j += 2) {
-            const uint32_t pk = pack_bf16x2(acc[4 * i + j], acc[4 * i + j + 1]);
-            sb[32 * b + 8 * i + j] = (uint16_t)pk;
-            sb[32 * b + 8 * i + j + 1] = (uint16_t)(pk >> 16);
-          }
+        for (int i = 0; i < 4; ++i)   // indices 32b + 8i + 4*half .. +3: element offset 32b + 8i
+          sb[(32 * b + 8 * i) / 4] = u32x2_t{pack_bf16x2(acc[4 * i], acc[4 * i + 1]),
+                                             pack_bf16x2(acc[4 * i + 2], acc[4 * i + 3])};
       }
     }
   };
