@@ -149,22 +149,21 @@ constexpr unsigned waitcnt_vm0_lgkm0 = 7u << 4;
 
 // Fused stage layout: two parts of 16 query rows.  Row r of part hi starts at
 // element h1*hi + 32 + 105*r and holds distance index e (0..63 in use) at +e
-// (h1: 28 when the parts are separate slices, below; else 0 with part 1 =
+// (h1: 16 when the parts are separate slices, below; else 0 with part 1 =
 // part 0 + 16 rows).  The product for distance index idx = e + q of query
 // q = 16*hi + r is written at 32 + 104*r + (h1 - 16)*hi + idx, so a lane's
-// writes sit at fixed offsets from one per-lane base, and its runs of four
-// consecutive indices (idx = 4k .. 4k+3) are 8-byte aligned: one 8-byte store
-// each.  The indices a lane also computes outside 0..63 (-31..95) land in the
+// writes sit at fixed offsets from one per-lane base, and its runs of eight
+// consecutive indices (idx = 8k .. 8k+7) are 16-byte aligned: one 16-byte
+// store each.  The indices a lane also computes outside 0..63 (-31..95) land in the
 // unused elements 64..104 of its own or the previous row, or in the part's
 // head (writes and reads stay in elements 32..1700 of a separate slice).  A row starts on
 // an odd element when r is odd, so the lanes read their 8-element runs as
-// five 4-byte words and shift out one element.  The pitch and h1 put the
-// 8-byte stores and the 4-byte reads of every half-wave on distinct banks.
+// five 4-byte words and shift out one element.
 // The two parts are either one stage of 32 rows or, in 4-wave work-groups
 // over head_dim 128, the wave's own 4 KiB slices of the next K and V buffers,
 // which are free until the wave issues its loads of the next tile.
 constexpr int FUSED_ROW = 105;
-constexpr int FUSED_PART1 = 28;
+constexpr int FUSED_PART1 = 16;
 
 // Which matrices of a K/V tile a load issues, and which of the wave's writes
 // (J < 0: all of them).
@@ -195,13 +194,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   constexpr int DSUB = D / 32;                  // 32-row slabs of O^T
   constexpr int ROWS_PER_DMA = 512 / D;         // key rows per 1 KiB LDS write
   constexpr int DMA_PER_WAVE = BN * D / 512 / NW;  // 1 KiB writes per wave per matrix
-  // a fused stage part (writes up to element h1 - 16 + 32 + 15*104 + 4 + 95,
+  // a fused stage part (writes up to element h1 - 16 + 32 + 15*104 + 95,
   // reads up to h1 + 32 + 15*105 + 56 + 9) fits the wave's slice of a K or V buffer
   static_assert(!ALIAS || (DMA_PER_WAVE * 512 > FUSED_PART1 + 32 + 15 * (FUSED_ROW - 1) + 99 &&
                            DMA_PER_WAVE * 512 > FUSED_PART1 + 32 + 15 * FUSED_ROW + 65),
                 "stage part too large");
-  static_assert(FUSED_ROW % 4 == 1 && FUSED_ROW > 96 && (FUSED_PART1 - 16) % 4 == 0,
-                "fused stage: 8-byte aligned runs of four, rows apart by more than 96");
+  static_assert(FUSED_ROW % 8 == 1 && FUSED_ROW > 96 && FUSED_PART1 % 8 == 0,
+                "fused stage: 16-byte aligned runs of eight, rows apart by more than 96");
   // two K/V buffers as separate objects, so the compiler can tell that the
   // direct loads into one do not alias reads of the other
   __shared__ __align__(16) uint16_t k_lds0[BN * D], v_lds0[BN * D];
@@ -463,7 +462,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
     else return stage_w;
   };
   const int frow = ALIAS ? (col & 15) : col;
-  const int fw_off = 32 + (FUSED_ROW - 1) * frow + (ALIAS ? (FUSED_PART1 - 16) * (col >> 4) : 0) + 4 * half;
+  const int fw_off = 32 + (FUSED_ROW - 1) * frow + (ALIAS ? (FUSED_PART1 - 16) * (col >> 4) : 0) + 8 * half;
   const int fr_off = 32 + FUSED_ROW * frow + (ALIAS ? FUSED_PART1 * (col >> 4) : 0);
   // the row start's element parity: a run is read as five words from the
   // word holding its first element, shifted right by fr_shift bytes
@@ -557,18 +556,23 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
   };
   // Bias of tile s0 for this wave's 32 queries into its stage: C^T = W^T r^T
   // over 96 distance indices in three 32-row MFMA blocks (A = W^T rows from
-  // the buffer, B = r), rounded to bf16.  Register 4i+j of block b holds
-  // index idx = 32b + 8i + 4*half + j of query col, written at
-  // fw_off - 4*half + idx of the lane's stage part.
+  // the buffer, B = r), rounded to bf16.  Output row m of a block is A row m,
+  // which lane m loads from W^T row sigma(m) of the block: sigma swaps bits 2
+  // and 3 of m, so register 4i+j holds index idx = 32b + 16(i/2) + 8*half +
+  // 4(i%2) + j of query col, and registers 8k .. 8k+7 hold the eight
+  // consecutive indices 32b + 16k + 8*half + 0..7, written at
+  // fw_off - 8*half + idx of the lane's stage part.
   auto fuse_bias = [&](const uint16_t *wsl, uint16_t *part) {
     if constexpr (FUSED) {
-      // row 32*qb + 32*b + col, logical chunk 2*kk + half (the swizzle of a
-      // row depends on col only: 32 rows are whole swizzle periods)
-      const int wsw = wsl_swizzle<DR>(col);
-      const uint16_t *wa = wsl + (32 * qb + col) * DR;
-      // 8-byte stores of four consecutive indices (8-byte aligned)
-      typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
-      lds_u32x2_t *sb = (lds_u32x2_t *)(part + fw_off);
+      // row 32*qb + 32*b + sigma(col), logical chunk 2*kk + half (the
+      // swizzle of a row depends on the row mod 32 only); the 16 rows a
+      // 16-lane group reads are the same set as without sigma
+      const int arow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+      const int wsw = wsl_swizzle<DR>(arow);
+      const uint16_t *wa = wsl + (32 * qb + arow) * DR;
+      // 16-byte stores of eight consecutive indices (16-byte aligned)
+      typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+      lds_u32x4_t *sb = (lds_u32x4_t *)(part + fw_off);
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
         f32x16_t acc;
@@ -581,9 +585,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void prefill_bf16_kernel(PrefillAr
                                                         __builtin_bit_cast(bf16x8_t, rf[kk]), acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)   // indices 32b + 8i + 4*half .. +3: element offset 32b + 8i
-          sb[(32 * b + 8 * i) / 4] = u32x2_t{pack_bf16x2(acc[4 * i], acc[4 * i + 1]),
-                                             pack_bf16x2(acc[4 * i + 2], acc[4 * i + 3])};
+        for (int k = 0; k < 2; ++k)   // indices 32b + 16k + 8*half .. +7: element offset 32b + 16k
+          sb[(32 * b + 16 * k) / 8] = u32x4_t{pack_bf16x2(acc[8 * k], acc[8 * k + 1]),
+                                              pack_bf16x2(acc[8 * k + 2], acc[8 * k + 3]),
+                                              pack_bf16x2(acc[8 * k + 4], acc[8 * k + 5]),
+                                              pack_bf16x2(acc[8 * k + 6], acc[8 * k + 7])};
       }
     }
   };
