@@ -15,6 +15,12 @@ offsets, and checks on the CPU that:
   [total_tokens][Hq][rel_extent] puts there;
 * basing a wave's resource on its first query's row, which lies past the
   sequence for such waves, fails the first check (the model can tell).
+
+For the variant that forms the bias in the kernel, a second model follows
+one band tile's product through the stage: the 16-byte stores stay aligned
+and inside the stage part, and every element a lane reads back was written
+by exactly one lane, with the value its query and distance name.  Without
+the product's row permutation, the read-back fails.
 """
 import random
 
@@ -139,3 +145,83 @@ def test_model_catches_a_resource_past_the_sequence():
     # starts past the tensor
     outside, _ = check(8, 8, 64, 0, [1500, 700], [333, 64], base_on_first_query=True)
     assert outside > 0
+
+
+# ---- fused variant: the stage the bias product is written to and read from ----
+# (prefill_bf16.hip: rows of 105 elements; part 1 of a separate 4 KiB slice 16
+# elements in, else 16 rows after part 0; lane m of the product loads W^T row
+# sigma(m), sigma swapping bits 2 and 3; 16-byte stores of 8 consecutive
+# indices; 8-element runs read back as five 4-byte words shifted by the row
+# start's parity.)
+FUSED_ROW, FUSED_PART1, SLICE = 105, 16, 2048
+
+
+def _sigma(m):
+    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1)
+
+
+def fused_stage_model(alias):
+    """Simulate one band tile's stage writes and reads for the 64 lanes of a
+    wave. Returns (per part: element -> every (query, idx) written there,
+    the runs each lane reads, the store addresses)."""
+    parts = [dict(), dict()]
+    stores = []
+    for lane in range(64):
+        col, half = lane & 31, lane >> 5
+        hi = col >> 4
+        frow = (col & 15) if alias else col
+        part = hi if alias else 0
+        fw_off = 32 + (FUSED_ROW - 1) * frow + ((FUSED_PART1 - 16) * hi if alias else 0) + 8 * half
+        for b in range(3):
+            for k in range(2):
+                base = fw_off + 32 * b + 16 * k
+                stores.append((part, base))
+                for x in range(8):
+                    # register 8k + x of block b: output row m = 8i + 4*half + j,
+                    # which the lane loaded from W^T row sigma(m)
+                    i, j = 2 * k + x // 4, x % 4
+                    idx = 32 * b + _sigma(8 * i + 4 * half + j)
+                    parts[part].setdefault(base + x, []).append((col, idx))
+    reads = {}
+    for lane in range(64):
+        col, half = lane & 31, lane >> 5
+        hi = col >> 4
+        frow = (col & 15) if alias else col
+        part = hi if alias else 0
+        fr_off = 32 + FUSED_ROW * frow + (FUSED_PART1 * hi if alias else 0)
+        for p in range(4):
+            word = fr_off // 2 + (7 - half - 2 * p) * 4
+            shift = fr_off & 1                      # elements shifted out
+            elems = [2 * word + shift + x for x in range(8)]
+            reads[(lane, p)] = (part, elems, [parts[part].get(e, []) for e in elems])
+    return parts, reads, stores
+
+
+@pytest.mark.parametrize("alias", [True, False])
+def test_fused_stage_layout(alias):
+    parts, reads, stores = fused_stage_model(alias)
+    limit = SLICE if alias else 32 + 32 * FUSED_ROW
+    for part, base in stores:
+        assert base % 8 == 0                        # 16-byte aligned stores
+        assert 0 <= base and base + 8 <= limit
+    for (lane, p), (part, elems, got) in reads.items():
+        col, half = lane & 31, lane >> 5
+        assert 0 <= min(elems) and max(elems) // 2 * 2 + 2 <= limit   # five words inside
+        # run p holds distance indices e = 63 - 8*half - 16p - 7 .. - 0 of the
+        # lane's query row, i.e. product index idx = e + q (ascending)
+        e0 = (7 - half - 2 * p) * 8
+        # exactly one lane writes each element read, with the right value
+        assert got == [[(col, e0 + x + col)] for x in range(8)], (lane, p)
+
+
+def test_fused_stage_model_catches_a_wrong_row_order():
+    # without the bit swap the product rows' order no longer matches the
+    # 16-byte stores: the reads then return other indices
+    global _sigma
+    keep = _sigma
+    _sigma = lambda m: m
+    try:
+        with pytest.raises(AssertionError):
+            test_fused_stage_layout(True)
+    finally:
+        _sigma = keep
