@@ -14,8 +14,10 @@
 // heads of one KV head times NW/hpw blocks of 32 consecutive queries; each
 // wave owns 32 queries of one head and every K/V tile it loads serves all
 // 32*NW (head, query) rows:
-//  * 64-key K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4,
-//    no register staging) into two buffers, row-major with XOR-swizzled
+//  * 64-key K and V tiles go HBM -> LDS directly (buffer_load_dwordx4 with
+//    the LDS bit through a buffer resource where a page holds whole tiles,
+//    else global_load_lds_dwordx4; no register staging) into two buffers,
+//    row-major with XOR-swizzled
 //    16-byte chunks: tile i+1 streams in while tile i computes, one barrier
 //    per tile.  Tile rows outside the work-group's key range (below the
 //    first key any of its queries sees, or past the end of the sequence)
@@ -31,8 +33,8 @@
 //    transposing LDS read ds_read_b64_tr_b16;
 //  * for each tile a query row needs the 64 distances t-s0-63 .. t-s0 of its
 //    bias row.  Each wave streams them for its 32 rows straight into a 4 KiB
-//    LDS stage of its own (global_load_lds_dwordx4, eight lanes per row, so
-//    a load instruction touches 8 rows instead of 32), one tile ahead, and
+//    LDS stage of its own (buffer loads with the LDS bit, eight lanes per
+//    row, so a load instruction touches 8 rows instead of 32), one tile ahead, and
 //    every lane then picks its four runs of 8 consecutive distances out of
 //    it with aligned 16-byte reads; every bias element crosses HBM once.
 //    Tiles whose distances all lie at or beyond R-1 use the single clamped
@@ -54,8 +56,9 @@
 // ([R][d_rel], distance-major) for the distances its queries meet, clamped to
 // [0, R-1]; each wave with a band tile multiplies them by its 32 r rows on the
 // matrix cores (3 x d_rel/16 MFMAs give the 96 distances of its 32 queries),
-// rounds the products to bf16 and writes them skewed into its stage, so that
-// the same aligned stage reads as above hand each lane its four runs.  Tiles
+// rounds the products to bf16 and writes them skewed into its stage, eight
+// consecutive distances per 16-byte store; each lane then reads its four runs
+// back as 4-byte words, shifted by one element on odd rows.  Tiles
 // at or beyond R-1 use r . W[:,R-1], formed once per row in fp32 and rounded
 // to bf16 like the stage entries: every bias value is the product rounded
 // once to bf16, the tensor a materialised bf16 bias would hold.
