@@ -138,8 +138,9 @@ typedef struct rba_attn_params {
  * sm_scale is not finite and positive, or max_seqlen exceeds
  * max_pages_per_seq * page_size.  RBA_ERR_UNSUPPORTED for a head_dim or
  * page_size outside the ranges above, or (bf16) for one pool page of all KV
- * heads, Hkv * page_size * head_dim * 2 bytes, above 4 GiB - 1, or for
- * max_pages_per_seq * page_size of 2^29 keys or more.
+ * heads, Hkv * page_size * head_dim * 2 bytes, above 4 GiB - 1, for
+ * max_pages_per_seq * page_size of 2^29 keys or more, or (bf16) for 32 bias
+ * rows of one head, (31 * Hq + 1) * rel_extent elements, of 2 GiB or more.
  * total_tokens == 0 or num_seqs == 0 is a no-op returning RBA_OK.
  */
 rba_status rba_prefill(const void *q, const int32_t *cu_seqlens,

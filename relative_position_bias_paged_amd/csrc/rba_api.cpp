@@ -6,6 +6,7 @@
 // caller's stream.  Nothing here allocates, frees or synchronises.
 #include "rba.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -170,8 +171,12 @@ rba_status prefill_impl(const void *q, const int32_t *cu_seqlens, int32_t total_
   if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return RBA_ERR_INVALID_ARG;
   if ((long long)max_seqlen > (long long)pt->max_pages_per_seq * pt->page_size)
     return RBA_ERR_INVALID_ARG;
-  // key positions stay below 2^29 (the bias stage's offsets rely on it)
+  // key positions stay below 2^29, and a wave's 32 bias rows (Hq * rel_extent
+  // elements apart) span under 2 GiB: the bias stage's 32-bit offsets rely on both
   if ((long long)pt->max_pages_per_seq * pt->page_size >= (1LL << 29)) return RBA_ERR_UNSUPPORTED;
+  if (!fused && kv->dtype == RBA_BF16 &&
+      (31LL * params->num_q_heads * params->rel_extent + params->rel_extent + 256) * 2 > INT_MAX)
+    return RBA_ERR_UNSUPPORTED;
 
   rba::PrefillArgs a{};
   a.q = q;

@@ -111,6 +111,13 @@ def test_prefill_key_positions_below_2_pow_29():
     assert _prefill_fused(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED
 
 
+def test_prefill_bias_rows_of_a_wave_within_2_gib():
+    # 32 rows of one head span (31 * Hq + 1) * R elements: refused when that
+    # reaches 2 GiB, before any launch (the fused variant reads no bias tensor)
+    kv, pt, prm = _layer(hq=64, hkv=8, R=1 << 20)
+    assert _prefill(kv, pt, prm) == rba.RBA_ERR_UNSUPPORTED
+
+
 def test_prefill_empty_is_noop():
     kv, pt, prm = _layer()
     assert _prefill(kv, pt, prm, q=0, cu=0, bias=0, out=0, T=0) == rba.RBA_OK
